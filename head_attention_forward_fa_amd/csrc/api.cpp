@@ -1,0 +1,258 @@
+// The C ABI of include/mha_fwd.h: argument validation (before any HIP call),
+// the per-(device, stream) scheduler workspace, and dispatch to the compiled
+// kernel variants.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "kernels.h"
+#include "mha_fwd.h"
+
+namespace mha {
+
+const Variant* find_variant(int dtype, int dn, int dr, int dv) {
+  switch (dtype) {
+    case MHA_DTYPE_F32:
+      return find_variant_f32(dn, dr, dv);
+    case MHA_DTYPE_BF16:
+      return find_variant_bf16(dn, dr, dv);
+    case MHA_DTYPE_FP8_E4M3:
+      return find_variant_fp8(dn, dr, dv);
+    default:
+      return nullptr;
+  }
+}
+
+}  // namespace mha
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return MHA_ERR_HIP;
+}
+
+// Scheduler workspace: [SchedState | table (int2 x capacity) | scratch (int x groups)]
+struct Workspace {
+  char* buf = nullptr;
+  size_t bytes = 0;
+};
+
+std::mutex g_mu;
+std::map<std::pair<int, void*>, Workspace> g_ws;
+
+constexpr size_t kStateBytes = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Returns the workspace of (dev, stream) with at least `need` bytes.  A
+// workspace that must grow is freed only after the stream has drained, since
+// kernels already queued on it may still read it.
+hipError_t get_workspace(int dev, hipStream_t stream, size_t need, char** out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  Workspace& ws = g_ws[{dev, (void*)stream}];
+  if (ws.bytes < need) {
+    if (ws.buf) {
+      hipError_t e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return e;
+      e = hipFree(ws.buf);
+      if (e != hipSuccess) return e;
+      ws.buf = nullptr;
+      ws.bytes = 0;
+    }
+    size_t bytes = align_up(need < (1u << 20) ? (1u << 20) : need, 1u << 20);
+    hipError_t e = hipMalloc(&ws.buf, bytes);
+    if (e != hipSuccess) return e;
+    ws.bytes = bytes;
+  }
+  *out = ws.buf;
+  return hipSuccess;
+}
+
+int cu_count(int dev) {
+  static int counts[64] = {0};
+  if (dev < 0 || dev >= 64) return 256;
+  if (counts[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+      n = 256;
+    counts[dev] = n;
+  }
+  return counts[dev];
+}
+
+struct Plan {
+  int capacity;  // work-table entries (upper bound on items)
+  int groups;    // batch * num_kv_heads
+  size_t bytes;  // workspace size
+};
+
+int make_plan(int batch, int max_seqlen, int num_heads, int num_kv_heads, int block_m,
+              Plan* plan) {
+  long long tiles = ((long long)max_seqlen + block_m - 1) / block_m;
+  long long cap = (long long)num_heads * batch * tiles;
+  if (tiles >= mha::kMaxQTilesPerSeq || cap > INT_MAX / 2)
+    return fail(MHA_ERR_INVALID_ARG, "problem too large for the work table");
+  long long groups = (long long)batch * num_kv_heads;
+  if (groups > INT_MAX / 2) return fail(MHA_ERR_INVALID_ARG, "batch * num_kv_heads too large");
+  plan->capacity = (int)cap;
+  plan->groups = (int)groups;
+  plan->bytes = kStateBytes + align_up((size_t)cap * sizeof(int2), 256) +
+                align_up((size_t)groups * sizeof(int), 256);
+  return MHA_OK;
+}
+
+int check_common(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                 int32_t num_heads, int32_t num_kv_heads) {
+  if (!cu_seqlens) return fail(MHA_ERR_INVALID_ARG, "cu_seqlens is NULL");
+  if (batch < 1) return fail(MHA_ERR_INVALID_ARG, "batch must be >= 1");
+  if (max_seqlen < 0) return fail(MHA_ERR_INVALID_ARG, "max_seqlen must be >= 0");
+  if (num_heads < 1 || num_kv_heads < 1)
+    return fail(MHA_ERR_INVALID_ARG, "num_heads and num_kv_heads must be >= 1");
+  if (num_heads % num_kv_heads != 0)
+    return fail(MHA_ERR_INVALID_ARG, "num_heads must be a multiple of num_kv_heads");
+  if (num_heads >= mha::kMaxHeads) return fail(MHA_ERR_INVALID_ARG, "num_heads too large");
+  return MHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mha_fwd_last_error(void) { return g_err.c_str(); }
+
+int mha_fwd_supported(int32_t dtype, int32_t head_dim_nope, int32_t head_dim_rope,
+                      int32_t v_dim) {
+  return mha::find_variant(dtype, head_dim_nope, head_dim_rope, v_dim) != nullptr;
+}
+
+int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen, int32_t num_heads,
+            int32_t num_kv_heads, int32_t head_dim_nope, int32_t head_dim_rope, int32_t v_dim,
+            const void* q_rope, const void* k_rope, int32_t causal, float softmax_scale,
+            int32_t dtype, const float* q_scale, const float* k_scale, void* stream) {
+  g_err.clear();
+  if (!q || !k || !v || !o || !lse) return fail(MHA_ERR_INVALID_ARG, "q, k, v, o, lse must be non-NULL");
+  int rc = check_common(cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads);
+  if (rc) return rc;
+  if (head_dim_nope < 1 || head_dim_rope < 0 || v_dim < 1)
+    return fail(MHA_ERR_INVALID_ARG, "head dims must be positive (rope >= 0)");
+  if ((q_rope == nullptr) != (k_rope == nullptr))
+    return fail(MHA_ERR_INVALID_ARG, "q_rope and k_rope must both be given or both NULL");
+  if ((head_dim_rope > 0) != (q_rope != nullptr))
+    return fail(MHA_ERR_INVALID_ARG, "rope pointers must be given iff head_dim_rope > 0");
+  if (causal != 0 && causal != 1) return fail(MHA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (dtype != MHA_DTYPE_F32 && dtype != MHA_DTYPE_BF16 && dtype != MHA_DTYPE_FP8_E4M3)
+    return fail(MHA_ERR_INVALID_ARG, "unknown dtype");
+  const bool fp8 = dtype == MHA_DTYPE_FP8_E4M3;
+  if (fp8 != (q_scale != nullptr) || fp8 != (k_scale != nullptr))
+    return fail(MHA_ERR_INVALID_ARG, "q_scale and k_scale must be given iff dtype is FP8_E4M3");
+  if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
+    return fail(MHA_ERR_INVALID_ARG, "softmax_scale must be finite");
+  const mha::Variant* var = mha::find_variant(dtype, head_dim_nope, head_dim_rope, v_dim);
+  if (!var) return fail(MHA_ERR_UNSUPPORTED, "no compiled kernel for this (dtype, Dn, Dr, Dv)");
+  if (max_seqlen == 0) return MHA_OK;
+
+  Plan plan;
+  rc = make_plan(batch, max_seqlen, num_heads, num_kv_heads, var->block_m, &plan);
+  if (rc) return rc;
+
+  const float sigma =
+      softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)(head_dim_nope + head_dim_rope));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  char* ws = nullptr;
+  e = get_workspace(dev, s, plan.bytes, &ws);
+  if (e != hipSuccess) return fail_hip(e, "workspace allocation");
+  auto* st = reinterpret_cast<mha::SchedState*>(ws);
+  auto* table = reinterpret_cast<int2*>(ws + kStateBytes);
+  auto* scratch = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(int2), 256));
+
+  e = mha::launch_prepass(cu_seqlens, batch, num_heads, num_kv_heads, causal, var->block_m,
+                          var->block_n, plan.capacity, table, st, scratch, s);
+  if (e != hipSuccess) return fail_hip(e, "scheduler prepass launch");
+
+  mha::AttnParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.q_rope = q_rope;
+  p.k_rope = k_rope;
+  p.q_scale = q_scale;
+  p.k_scale = k_scale;
+  p.cu_seqlens = cu_seqlens;
+  p.table = table;
+  p.sched = st;
+  p.batch = batch;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_heads / num_kv_heads;
+  p.causal = causal;
+  p.scale_log2 = sigma * 1.4426950408889634f;
+
+  long long grid = (long long)cu_count(dev) * var->blocks_per_cu();
+  if (grid > plan.capacity) grid = plan.capacity;
+  if (grid < 1) grid = 1;
+  e = var->launch(p, (int)grid, s);
+  if (e != hipSuccess) return fail_hip(e, "attention kernel launch");
+  return MHA_OK;
+}
+
+int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                    int32_t num_heads, int32_t num_kv_heads, int32_t causal, int32_t block_m,
+                    int32_t grid, int32_t* visits, void* stream) {
+  g_err.clear();
+  int rc = check_common(cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads);
+  if (rc) return rc;
+  if (!visits) return fail(MHA_ERR_INVALID_ARG, "visits is NULL");
+  if (causal != 0 && causal != 1) return fail(MHA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  int block_n;
+  if (block_m == mha::kBlockM_Mfma)
+    block_n = mha::kBlockN_Mfma;
+  else if (block_m == mha::kBlockM_F32)
+    block_n = mha::kBlockN_F32;
+  else
+    return fail(MHA_ERR_INVALID_ARG, "block_m must be 64 or 128");
+  if (grid < 0) return fail(MHA_ERR_INVALID_ARG, "grid must be >= 0");
+  if (max_seqlen == 0) return MHA_OK;
+  Plan plan;
+  rc = make_plan(batch, max_seqlen, num_heads, num_kv_heads, block_m, &plan);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  char* ws = nullptr;
+  e = get_workspace(dev, s, plan.bytes, &ws);
+  if (e != hipSuccess) return fail_hip(e, "workspace allocation");
+  auto* st = reinterpret_cast<mha::SchedState*>(ws);
+  auto* table = reinterpret_cast<int2*>(ws + kStateBytes);
+  auto* scratch = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(int2), 256));
+  e = mha::launch_prepass(cu_seqlens, batch, num_heads, num_kv_heads, causal, block_m, block_n,
+                          plan.capacity, table, st, scratch, s);
+  if (e != hipSuccess) return fail_hip(e, "scheduler prepass launch");
+  if (grid == 0) grid = cu_count(dev) * 2;
+  const int tiles = (int)(((long long)max_seqlen + block_m - 1) / block_m);
+  e = mha::launch_sched_visit(cu_seqlens, batch, num_heads, tiles, table, st, visits, grid, s);
+  if (e != hipSuccess) return fail_hip(e, "visit kernel launch");
+  return MHA_OK;
+}
+
+}  // extern "C"

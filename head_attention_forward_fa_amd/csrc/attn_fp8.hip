@@ -1,0 +1,17 @@
+// fp8 (OCP E4M3 Q/K with per-token scales, bf16 V) instantiation of the
+// matrix-core attention kernel.
+#include "attn_mfma.h"
+
+namespace mha {
+namespace {
+using C128 = MfmaCfg<128, 0, 128, true>;
+const Variant kFp8[] = {
+    {launch_mfma<C128>, blocks_mfma<C128>, C128::BM, C128::BN},
+};
+}  // namespace
+
+const Variant* find_variant_fp8(int dn, int dr, int dv) {
+  if (dn == 128 && dr == 0 && dv == 128) return &kFp8[0];
+  return nullptr;
+}
+}  // namespace mha

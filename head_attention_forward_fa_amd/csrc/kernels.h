@@ -1,0 +1,43 @@
+// Host-side launchers of the device kernels (internal to the library; the
+// public C ABI is include/mha_fwd.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace mha {
+
+// Query-tile heights of the two kernel families (rows of Q per work item).
+constexpr int kBlockM_Mfma = 128;
+constexpr int kBlockN_Mfma = 64;
+constexpr int kBlockM_F32 = 64;
+constexpr int kBlockN_F32 = 32;
+
+hipError_t launch_prepass(const int32_t* cu, int batch, int num_heads, int num_kv_heads,
+                          int causal, int bm, int bn, int capacity, int2* table,
+                          SchedState* st, int* scratch, hipStream_t stream);
+
+hipError_t launch_sched_visit(const int32_t* cu, int batch, int num_heads, int tiles,
+                              const int2* table, SchedState* st, int* visits, int grid,
+                              hipStream_t stream);
+
+// A kernel variant: its launcher and its occupancy (resident workgroups per
+// CU at its LDS and register footprint, computed once per device).
+struct Variant {
+  hipError_t (*launch)(const AttnParams& p, int grid, hipStream_t stream);
+  int (*blocks_per_cu)();
+  int block_m;
+  int block_n;
+};
+
+// Lookup of the compiled variant for (dtype, Dn, Dr, Dv); nullptr if none.
+const Variant* find_variant(int dtype, int dn, int dr, int dv);
+
+// Per-family tables (defined next to each kernel family).
+const Variant* find_variant_f32(int dn, int dr, int dv);
+const Variant* find_variant_bf16(int dn, int dr, int dv);
+const Variant* find_variant_fp8(int dn, int dr, int dv);
+
+}  // namespace mha

@@ -1,0 +1,134 @@
+"""PyTorch-facing binding of the C ABI (same names as include/mha_fwd.h).
+
+PyTorch supplies device memory and the current stream; the tensors' data
+pointers go straight to the library, which does all of the computation.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _native as nat
+
+
+def _dtype_code(q: torch.Tensor) -> int:
+    if q.dtype == torch.float32:
+        return nat.MHA_DTYPE_F32
+    if q.dtype == torch.bfloat16:
+        return nat.MHA_DTYPE_BF16
+    if q.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return nat.MHA_DTYPE_FP8_E4M3
+    raise ValueError(f"unsupported q dtype {q.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: Optional[torch.Tensor], name: str, device, dtype=None, shape=None):
+    if t is None:
+        return
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def mha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+            causal: bool = False,
+            cu_seqlens: Optional[torch.Tensor] = None,
+            max_seqlen: Optional[int] = None,
+            q_rope: Optional[torch.Tensor] = None,
+            k_rope: Optional[torch.Tensor] = None,
+            q_scale: Optional[torch.Tensor] = None,
+            k_scale: Optional[torch.Tensor] = None,
+            softmax_scale: Optional[float] = None,
+            out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Fused attention forward; returns (o, lse).
+
+    q [T, Hq, Dn], k [T, Hkv, Dn], v [T, Hkv, Dv] with cu_seqlens (int32
+    [B+1], on the device) and max_seqlen; or q [B, S, Hq, Dn] etc. for a dense
+    batch (no cu_seqlens).  o has q's leading shape with Dv columns; lse is
+    [Hq, T] float32 (natural log).  fp8: q, k as float8_e4m3fn (or uint8
+    codes) with q_scale [T, Hq] and k_scale [T, Hkv] float32; v bf16.
+    """
+    dense = q.dim() == 4
+    if dense:
+        if cu_seqlens is not None:
+            raise ValueError("cu_seqlens is for packed [T, H, D] inputs")
+        B, S = q.shape[0], q.shape[1]
+        flat = lambda t: None if t is None else t.reshape(B * S, *t.shape[2:])
+        qf, kf, vf = flat(q), flat(k), flat(v)
+        qrf, krf = flat(q_rope), flat(k_rope)
+        qsf, ksf = flat(q_scale), flat(k_scale)
+        cu = torch.arange(0, (B + 1) * S, S, dtype=torch.int32, device=q.device)
+        max_seqlen = S
+    else:
+        if cu_seqlens is None or max_seqlen is None:
+            raise ValueError("packed inputs need cu_seqlens and max_seqlen")
+        qf, kf, vf, qrf, krf, qsf, ksf = q, k, v, q_rope, k_rope, q_scale, k_scale
+        cu = cu_seqlens
+        B = cu.numel() - 1
+    if qf.dim() != 3 or kf.dim() != 3 or vf.dim() != 3:
+        raise ValueError("q, k, v must be [T, H, D] (or [B, S, H, D])")
+    dev = qf.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    code = _dtype_code(qf)
+    T, Hq, Dn = qf.shape
+    Hkv, Dv = kf.shape[1], vf.shape[2]
+    Dr = 0 if qrf is None else qrf.shape[2]
+    vdt = torch.float32 if code == nat.MHA_DTYPE_F32 else torch.bfloat16
+    _need(qf, "q", dev)
+    _need(kf, "k", dev, qf.dtype, (T, Hkv, Dn))
+    _need(vf, "v", dev, vdt, (T, Hkv, Dv))
+    _need(qrf, "q_rope", dev, vdt, (T, Hq, Dr) if Dr else None)
+    _need(krf, "k_rope", dev, vdt, (T, Hkv, Dr) if Dr else None)
+    _need(qsf, "q_scale", dev, torch.float32, (T, Hq) if qsf is not None else None)
+    _need(ksf, "k_scale", dev, torch.float32, (T, Hkv) if ksf is not None else None)
+    _need(cu, "cu_seqlens", dev, torch.int32, (B + 1,))
+    o = out if out is not None else torch.empty((T, Hq, Dv), dtype=vdt, device=dev)
+    _need(o, "out", dev, vdt, (T, Hq, Dv))
+    lse_t = lse if lse is not None else torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    _need(lse_t, "lse", dev, torch.float32, (Hq, T))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    lib = nat.load()
+    with torch.cuda.device(dev):
+        st = lib.mha_fwd(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(o), _ptr(lse_t),
+                         _ptr(cu), int(B), int(max_seqlen), int(Hq), int(Hkv),
+                         int(Dn), int(Dr), int(Dv), _ptr(qrf), _ptr(krf),
+                         int(bool(causal)),
+                         float(softmax_scale) if softmax_scale is not None else 0.0,
+                         code, _ptr(qsf), _ptr(ksf), stream)
+    nat.check(st)
+    if dense:
+        o = o.view(B, S, Hq, Dv)
+    return o, lse_t
+
+
+def mha_fwd_supported(dtype_code: int, head_dim_nope: int, head_dim_rope: int, v_dim: int) -> bool:
+    return bool(nat.load().mha_fwd_supported(dtype_code, head_dim_nope, head_dim_rope, v_dim))
+
+
+def mha_sched_visit(cu_seqlens: torch.Tensor, max_seqlen: int, num_heads: int,
+                    num_kv_heads: int, causal: bool, block_m: int = 128,
+                    grid: int = 0) -> torch.Tensor:
+    """Runs the scheduler alone; returns visit counts [Hq, B, tiles] (int32)."""
+    B = cu_seqlens.numel() - 1
+    tiles = (max_seqlen + block_m - 1) // block_m
+    visits = torch.zeros((num_heads, B, max(tiles, 1)), dtype=torch.int32,
+                         device=cu_seqlens.device)
+    stream = torch.cuda.current_stream(cu_seqlens.device).cuda_stream
+    with torch.cuda.device(cu_seqlens.device):
+        st = nat.load().mha_sched_visit(_ptr(cu_seqlens), int(B), int(max_seqlen),
+                                        int(num_heads), int(num_kv_heads), int(bool(causal)),
+                                        int(block_m), int(grid), _ptr(visits), stream)
+    nat.check(st)
+    return visits

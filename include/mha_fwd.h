@@ -1,0 +1,150 @@
+/*
+ * mha_fwd.h -- C ABI of the fused multi-head-attention forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  For every sequence b of a ragged batch, every query head
+ * h and every query row i of that sequence:
+ *
+ *     S[i, j] = sigma * (q[i, h, :Dn] . k[j, g, :Dn] + q_rope[i, h, :] . k_rope[j, g, :])
+ *     O[i, h, :] = sum_j softmax_j(S[i, .]) v[j, g, :]          over visible keys j
+ *     LSE[h, i] = ln sum_j exp(S[i, j])                          over visible keys j
+ *
+ * with g = h / (num_heads / num_kv_heads) (grouped-query attention) and key j
+ * visible to query i iff j < L_b and, when causal, j <= i (indices local to
+ * the sequence; queries and keys share one length per sequence).
+ *
+ * The pages this follows (the Modular API pages "SM100AttentionSMem",
+ * "TMAProducerPipeline" and "MHATileScheduler" for an SM100 flash-attention
+ * kernel) give the pieces: Q/K split into a "nope" part and a separately
+ * typed "rope" part and an optional per-token scale for Q and K
+ * (SM100AttentionSMem, Parameters); per-batch sequence-length offsets
+ * (MHATileScheduler, Required methods: get_current_work_info); a per-row
+ * correction buffer for the online softmax (SM100AttentionSMem, Methods:
+ * correction_smem).  The signature itself is this library's own.
+ *
+ * Conventions for every entry point below:
+ *   - tensor pointers are DEVICE pointers to contiguous, token-major ("THD")
+ *     arrays; the caller owns them; the library keeps no reference after the
+ *     call returns;
+ *   - calls are asynchronous on `stream` (a hipStream_t, passed as void*;
+ *     NULL = the null stream); outputs are valid once the stream reaches
+ *     them;
+ *   - on any nonzero status nothing has been launched and the outputs are
+ *     untouched; mha_fwd_last_error() returns a message for the calling
+ *     thread's last nonzero status.
+ */
+#ifndef MHA_FWD_H_
+#define MHA_FWD_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  F32: q, k, v, q_rope, k_rope and o are float32.
+ * BF16: all of them are bfloat16.  FP8_E4M3: q and k are OCP E4M3 codes
+ * ("fn", largest finite 448) with float32 per-token scales; v, o are
+ * bfloat16 (SM100AttentionSMem, Parameters: qkv_dtype, scale_dtype_). */
+typedef enum {
+  MHA_DTYPE_F32 = 0,
+  MHA_DTYPE_BF16 = 1,
+  MHA_DTYPE_FP8_E4M3 = 2
+} mha_dtype_t;
+
+typedef enum {
+  MHA_OK = 0,
+  MHA_ERR_INVALID_ARG = 1,  /* a pointer, size or flag is malformed            */
+  MHA_ERR_UNSUPPORTED = 2,  /* (dtype, Dn, Dr, Dv) outside the compiled set      */
+  MHA_ERR_HIP = 3           /* a HIP runtime call or launch failed               */
+} mha_status_t;
+
+/*
+ * mha_fwd -- O and LSE for a ragged batch of sequences.
+ *
+ *   q           [T, num_heads, head_dim_nope]      element type per `dtype`
+ *   k           [T, num_kv_heads, head_dim_nope]
+ *   v           [T, num_kv_heads, v_dim]           float32 (F32) or bfloat16
+ *   o           [T, num_heads, v_dim]   written;   float32 (F32) or bfloat16
+ *   lse         [num_heads, T] float32, written;   natural log, softmax scale
+ *               included
+ *   cu_seqlens  [batch + 1] int32: cu_seqlens[0] = 0, nondecreasing, the
+ *               token offset of each sequence (MHATileScheduler, Required
+ *               methods: the optional pointer of per-batch sequence length
+ *               offsets).  T = cu_seqlens[batch].  Not checked on the host
+ *               (that would need a device sync).
+ *   batch       number of sequences, >= 1
+ *   max_seqlen  >= every sequence length; sizes the work table (num_heads *
+ *               batch * ceil(max_seqlen / 128) entries).  0 means every
+ *               sequence is empty: nothing is launched.  When the lengths
+ *               break this bound so far that the work items would not fit in
+ *               that table, the device refuses the whole call and writes
+ *               nothing.
+ *   num_heads, num_kv_heads   query and key/value heads; num_heads must be a
+ *               multiple of num_kv_heads
+ *   head_dim_nope, head_dim_rope, v_dim   Dn, Dr (0 = no rope part), Dv
+ *   q_rope      [T, num_heads, head_dim_rope], k_rope [T, num_kv_heads,
+ *               head_dim_rope]: the rope part of Q and K, already rotated,
+ *               bfloat16 (float32 for F32).  NULL iff head_dim_rope == 0
+ *               (SM100AttentionSMem, Parameters: rope_dtype_; Methods:
+ *               q_rope_smem).
+ *   causal      0: every key of the sequence is visible; 1: key j visible to
+ *               query i iff j <= i
+ *   softmax_scale  sigma; <= 0 selects 1/sqrt(head_dim_nope + head_dim_rope)
+ *   dtype       an mha_dtype_t
+ *   q_scale     [T, num_heads] float32, k_scale [T, num_kv_heads] float32:
+ *               dequantisation scales, value = code * scale, one per (token,
+ *               head) row, >= 0 (SM100AttentionSMem, Methods: q_scale_smem,
+ *               k_scale_smem).  Required iff dtype == FP8_E4M3, else NULL.
+ *   stream      hipStream_t or NULL
+ *
+ * Compiled set (MHA_ERR_UNSUPPORTED otherwise):
+ *   F32      (Dn, Dr, Dv) in {(64,0,64), (128,0,128), (128,64,128)}
+ *   BF16     (Dn, Dr, Dv) in {(64,0,64), (128,0,128), (128,64,128)}
+ *   FP8_E4M3 (Dn, Dr, Dv) in {(128,0,128)}
+ *
+ * The library owns a small workspace per (device, stream): the work table and
+ * queue counters of the persistent scheduler.  It is allocated on the first
+ * call for that pair (so the first call must not be inside a HIP graph
+ * capture) and grown when a larger problem arrives.  Calls on one stream are
+ * ordered and may follow each other freely; calls on two streams use two
+ * workspaces.
+ */
+int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+            int32_t num_heads, int32_t num_kv_heads,
+            int32_t head_dim_nope, int32_t head_dim_rope, int32_t v_dim,
+            const void* q_rope, const void* k_rope,
+            int32_t causal, float softmax_scale, int32_t dtype,
+            const float* q_scale, const float* k_scale, void* stream);
+
+/* Message for the calling thread's last nonzero status ("" if none).  The
+ * string is owned by the library and valid until the thread's next call. */
+const char* mha_fwd_last_error(void);
+
+/* 1 if (dtype, Dn, Dr, Dv) is in the compiled set, else 0.  No HIP call. */
+int mha_fwd_supported(int32_t dtype, int32_t head_dim_nope,
+                      int32_t head_dim_rope, int32_t v_dim);
+
+/*
+ * mha_sched_visit -- diagnostic for the persistent tile scheduler
+ * (MHATileScheduler: "maps work tiles to thread blocks, advances the per-CTA
+ * state through the work grid").  Builds the work table exactly as mha_fwd
+ * does for (cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads, causal,
+ * block_m) and runs `grid` workgroups (0 = the size mha_fwd would use for
+ * this block_m) that only fetch work items and add 1 to
+ * visits[h * (batch * tiles) + b * tiles + qtile], tiles =
+ * ceil(max_seqlen / block_m).  visits is a caller-owned device int32 array of
+ * num_heads * batch * tiles entries, zeroed by the caller.  block_m is 64 or
+ * 128 (the float32 and MFMA kernels' query tiles).  Every existing item must
+ * end with exactly one visit.
+ */
+int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                    int32_t num_heads, int32_t num_kv_heads, int32_t causal,
+                    int32_t block_m, int32_t grid, int32_t* visits, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHA_FWD_H_ */

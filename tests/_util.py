@@ -1,0 +1,115 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device, run the
+HIP path through the binding, and evaluate the oracle on the same inputs."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from mha_inputs import Inputs
+
+TOL_O = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
+TOL_LSE = 1e-3
+
+
+def device_tensors(inp: Inputs, device="cuda:0"):
+    def bits(a, dt):
+        if a is None:
+            return None
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        if dt == "fp8":
+            return torch.from_numpy(a).view(torch.float8_e4m3fn).to(device)
+        return torch.from_numpy(a).to(device)
+
+    qk_dt = inp.dtype
+    v_dt = "f32" if inp.dtype == "f32" else "bf16"
+    return dict(
+        q=bits(inp.q, qk_dt), k=bits(inp.k, qk_dt), v=bits(inp.v, v_dt),
+        q_rope=bits(inp.q_rope, v_dt), k_rope=bits(inp.k_rope, v_dt),
+        q_scale=None if inp.q_scale is None else torch.from_numpy(inp.q_scale).to(device),
+        k_scale=None if inp.k_scale is None else torch.from_numpy(inp.k_scale).to(device),
+        cu_seqlens=torch.from_numpy(inp.cu_seqlens).to(device),
+    )
+
+
+def run_gpu(inp: Inputs, device="cuda:0", tensors=None):
+    from head_attention_forward_fa_amd import mha_fwd
+    t = tensors or device_tensors(inp, device)
+    o, lse = mha_fwd(t["q"], t["k"], t["v"], causal=inp.causal, cu_seqlens=t["cu_seqlens"],
+                     max_seqlen=inp.max_seqlen, q_rope=t["q_rope"], k_rope=t["k_rope"],
+                     q_scale=t["q_scale"], k_scale=t["k_scale"],
+                     softmax_scale=inp.softmax_scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def decoded(inp: Inputs, lo: int = 0, hi: int | None = None):
+    """Oracle-side float64 values of tokens [lo, hi)."""
+    hi = inp.total_tokens if hi is None else hi
+    sl = slice(lo, hi)
+    if inp.dtype == "f32":
+        dec = lambda a: None if a is None else a[sl].astype(np.float64)
+        q, k = dec(inp.q), dec(inp.k)
+        v, qr, kr = dec(inp.v), dec(inp.q_rope), dec(inp.k_rope)
+    else:
+        dec = lambda a: None if a is None else oracle.decode_bf16(a[sl])
+        if inp.dtype == "fp8":
+            q = oracle.dequantize_per_token(inp.q[sl], inp.q_scale[sl])
+            k = oracle.dequantize_per_token(inp.k[sl], inp.k_scale[sl])
+        else:
+            q, k = dec(inp.q), dec(inp.k)
+        v, qr, kr = dec(inp.v), dec(inp.q_rope), dec(inp.k_rope)
+    return q, k, v, qr, kr
+
+
+def oracle_full(inp: Inputs):
+    q, k, v, qr, kr = decoded(inp)
+    return oracle.mha_forward(q, k, v, inp.cu_seqlens, inp.causal, inp.softmax_scale,
+                              q_rope=qr, k_rope=kr)
+
+
+def oracle_rows(inp: Inputs, tokens):
+    """Oracle O [n, Hq, Dv] and LSE [Hq, n] at the given global tokens,
+    decoding only the sequences that hold them."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    cu = inp.cu_seqlens.astype(np.int64)
+    o = np.empty((len(tokens), inp.num_heads, inp.v_dim))
+    lse = np.empty((inp.num_heads, len(tokens)))
+    seq = np.searchsorted(cu, tokens, side="right") - 1
+    for b in np.unique(seq):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        idx = np.nonzero(seq == b)[0]
+        q, k, v, qr, kr = decoded(inp, s0, s1)
+        ob, lb = oracle.mha_forward_rows(q, k, v, np.array([0, s1 - s0]), inp.causal,
+                                         tokens[idx] - s0, inp.softmax_scale,
+                                         q_rope=qr, k_rope=kr)
+        o[idx] = ob
+        lse[:, idx] = lb
+    return o, lse
+
+
+def sample_tokens(inp: Inputs, n_random: int = 24, seed: int = 1):
+    """First, last and tile-boundary rows of every sequence plus random ones."""
+    cu = inp.cu_seqlens.astype(np.int64)
+    rng = np.random.default_rng(seed)
+    toks = set()
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        if s1 == s0:
+            continue
+        for i in (0, 1, 63, 64, 127, 128, 129, s1 - s0 - 2, s1 - s0 - 1):
+            if 0 <= i < s1 - s0:
+                toks.add(s0 + i)
+    if inp.total_tokens:
+        toks.update(int(x) for x in rng.integers(0, inp.total_tokens, n_random))
+    return np.array(sorted(toks), dtype=np.int64)
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0

@@ -1,0 +1,111 @@
+"""The C ABI on the CPU: the library loads, exports what include/mha_fwd.h
+declares, and rejects malformed arguments before any HIP call."""
+
+import math
+import os
+import re
+
+import pytest
+
+from head_attention_forward_fa_amd import _native as nat
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for f in os.listdir(inc):
+        if f.endswith(".h"):
+            text = open(os.path.join(inc, f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names.update(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(mha_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    lib = nat.load()
+    names = declared_functions()
+    assert set(names) >= {"mha_fwd", "mha_fwd_last_error", "mha_fwd_supported", "mha_sched_visit"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(nat.EXPORTS) == set(names)
+
+
+def call(**over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu=FAKE, batch=1, max_seqlen=16,
+                hq=4, hkv=2, dn=128, dr=0, dv=128, q_rope=None, k_rope=None, causal=1,
+                scale=0.0, dtype=nat.MHA_DTYPE_BF16, q_scale=None, k_scale=None, stream=None)
+    args.update(over)
+    lib = nat.load()
+    return lib.mha_fwd(args["q"], args["k"], args["v"], args["o"], args["lse"], args["cu"],
+                       args["batch"], args["max_seqlen"], args["hq"], args["hkv"], args["dn"],
+                       args["dr"], args["dv"], args["q_rope"], args["k_rope"], args["causal"],
+                       args["scale"], args["dtype"], args["q_scale"], args["k_scale"],
+                       args["stream"])
+
+
+BAD = [
+    dict(q=None), dict(lse=None), dict(cu=None),
+    dict(batch=0), dict(max_seqlen=-1), dict(hq=0), dict(hkv=3), dict(hq=4096, hkv=1),
+    dict(dn=0), dict(dr=-1), dict(dv=0),
+    dict(dr=64),                                  # rope depth without rope pointers
+    dict(q_rope=FAKE, k_rope=FAKE),               # rope pointers without depth
+    dict(dr=64, q_rope=FAKE),                     # only one rope pointer
+    dict(causal=2), dict(dtype=7),
+    dict(dtype=nat.MHA_DTYPE_FP8_E4M3),           # fp8 without scales
+    dict(dtype=nat.MHA_DTYPE_FP8_E4M3, q_scale=FAKE),
+    dict(q_scale=FAKE, k_scale=FAKE),             # scales with bf16
+    dict(scale=math.nan), dict(scale=math.inf),
+]
+
+
+@pytest.mark.parametrize("over", BAD)
+def test_invalid_arguments_rejected(over):
+    assert call(**over) == nat.MHA_ERR_INVALID_ARG
+    assert nat.load().mha_fwd_last_error().decode()
+
+
+@pytest.mark.parametrize("over", [dict(dn=96, dv=96), dict(dv=64),
+                                  dict(dtype=nat.MHA_DTYPE_FP8_E4M3, q_scale=FAKE,
+                                       k_scale=FAKE, dn=64, dv=64),
+                                  dict(dtype=nat.MHA_DTYPE_FP8_E4M3, q_scale=FAKE,
+                                       k_scale=FAKE, dr=64, q_rope=FAKE, k_rope=FAKE)])
+def test_unsupported_shapes(over):
+    assert call(**over) == nat.MHA_ERR_UNSUPPORTED
+
+
+def test_zero_max_seqlen_is_a_no_op():
+    assert call(max_seqlen=0) == nat.MHA_OK
+    assert nat.load().mha_fwd_last_error().decode() == ""
+
+
+def test_supported_set():
+    lib = nat.load()
+    want = {
+        nat.MHA_DTYPE_F32: {(64, 0, 64), (128, 0, 128), (128, 64, 128)},
+        nat.MHA_DTYPE_BF16: {(64, 0, 64), (128, 0, 128), (128, 64, 128)},
+        nat.MHA_DTYPE_FP8_E4M3: {(128, 0, 128)},
+    }
+    for dt, shapes in want.items():
+        for dn in (32, 64, 96, 128, 192, 256):
+            for dr in (0, 32, 64):
+                for dv in (64, 128):
+                    assert bool(lib.mha_fwd_supported(dt, dn, dr, dv)) == ((dn, dr, dv) in shapes)
+
+
+def test_sched_visit_validation():
+    lib = nat.load()
+    assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 32, 0, FAKE, None) == nat.MHA_ERR_INVALID_ARG
+    assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 128, 0, None, None) == nat.MHA_ERR_INVALID_ARG
+    assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 128, -1, FAKE, None) == nat.MHA_ERR_INVALID_ARG
+    assert lib.mha_sched_visit(FAKE, 1, 0, 4, 2, 1, 128, 0, FAKE, None) == nat.MHA_OK
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    from head_attention_forward_fa_amd import mha_fwd
+    q = torch.zeros(2, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mha_fwd(q, q, q, cu_seqlens=torch.tensor([0, 2], dtype=torch.int32), max_seqlen=2)

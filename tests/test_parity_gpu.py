@@ -1,0 +1,165 @@
+"""HIP path vs the float64 oracle, element by element, through the C ABI.
+
+Small cases (seconds for the oracle) span several 128-row query tiles and
+64-key blocks with ragged tails, GQA, empty sequences, the nope/rope split and
+fp8; the five named workloads run at full size with the oracle evaluated on
+sampled rows (first, last, tile-boundary and random tokens, every head).
+Tolerances (max-abs): O 1e-4 fp32, 2e-2 bf16, 6e-2 fp8; LSE 1e-3.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mha_inputs as mi
+from _util import (TOL_LSE, TOL_O, device_tensors, max_abs, oracle_full, oracle_rows,
+                   run_gpu, sample_tokens, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # dtype, lengths, Hq, Hkv, Dn, Dr, Dv, causal
+    ("bf16", [300], 4, 4, 128, 0, 128, True),
+    ("bf16", [300], 4, 4, 128, 0, 128, False),
+    ("bf16", [1, 129, 0, 517, 64], 8, 2, 128, 0, 128, True),
+    ("bf16", [1, 129, 0, 517, 64], 8, 2, 128, 0, 128, False),
+    ("bf16", [200, 77], 4, 1, 64, 0, 64, True),
+    ("bf16", [200, 77], 4, 1, 64, 0, 64, False),
+    ("bf16", [333], 4, 4, 128, 64, 128, True),
+    ("bf16", [190, 5], 4, 2, 128, 64, 128, False),
+    ("fp8", [300, 50], 4, 4, 128, 0, 128, True),
+    ("fp8", [300, 50], 4, 4, 128, 0, 128, False),
+    ("fp8", [257], 8, 2, 128, 0, 128, True),
+    ("f32", [100, 3], 2, 2, 128, 0, 128, True),
+    ("f32", [70], 2, 1, 128, 64, 128, True),
+    ("f32", [130, 1], 2, 2, 64, 0, 64, True),
+    ("f32", [130, 1], 2, 2, 64, 0, 64, False),
+]
+
+
+def _check(inp, o, lse, ref_o, ref_lse, tokens=None):
+    o64, lse64 = to_f64(o), to_f64(lse)
+    if tokens is not None:
+        o64, lse64 = o64[tokens], lse64[:, tokens]
+    eo, el = max_abs(o64, ref_o), max_abs(lse64, ref_lse)
+    assert np.all(np.isfinite(o64)) and np.all(np.isfinite(lse64))
+    assert eo <= TOL_O[inp.dtype], f"{inp.name}: O max-abs {eo}"
+    assert el <= TOL_LSE, f"{inp.name}: LSE max-abs {el}"
+    return eo, el
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}x{c[3]}-{c[4]}+{c[5]}-{c[6]}-{'c' if c[7] else 'nc'}")
+def test_small_cases_match_oracle(case):
+    dt, lens, hq, hkv, dn, dr, dv, causal = case
+    inp = mi.make_inputs(dtype=dt, seqlens=lens, num_heads=hq, num_kv_heads=hkv,
+                         head_dim_nope=dn, head_dim_rope=dr, v_dim=dv, causal=causal,
+                         seed=7, name=str(case))
+    print("case", case, flush=True)
+    o, lse = run_gpu(inp)
+    ref_o, ref_lse = oracle_full(inp)
+    _check(inp, o, lse, ref_o, ref_lse)
+
+
+def test_fp32_dense_workload_full():
+    inp = mi.workload("fp32_b1_h2_s128_d64")
+    o, lse = run_gpu(inp)
+    ref_o, ref_lse = oracle_full(inp)
+    eo, el = _check(inp, o, lse, ref_o, ref_lse)
+    print(f"fp32 workload: O err {eo:.3e}, LSE err {el:.3e}")
+
+
+@pytest.mark.parametrize("name", mi.WORKLOAD_ORDER[1:])
+def test_full_size_workloads_sampled(name):
+    print("workload", name, flush=True)
+    inp = mi.workload(name)
+    o, lse = run_gpu(inp)
+    # every row of every head is finite; sampled rows match the oracle
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    toks = sample_tokens(inp)
+    ref_o, ref_lse = oracle_rows(inp, toks)
+    eo, el = _check(inp, o, lse, ref_o, ref_lse, tokens=toks)
+    print(f"{name}: {len(toks)} tokens x {inp.num_heads} heads, O err {eo:.3e}, LSE err {el:.3e}")
+
+
+def test_dense_layout_equals_packed():
+    inp = mi.make_inputs(dtype="bf16", seqlens=[256, 256], num_heads=4, num_kv_heads=2,
+                         head_dim_nope=128, v_dim=128, causal=True, seed=3)
+    from head_attention_forward_fa_amd import mha_fwd
+    t = device_tensors(inp)
+    o1, l1 = run_gpu(inp, tensors=t)
+    r = lambda x: x.view(2, 256, *x.shape[1:])
+    o2, l2 = mha_fwd(r(t["q"]), r(t["k"]), r(t["v"]), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2.reshape_as(o1)) and torch.equal(l1, l2)
+
+
+def test_repeat_calls_are_bitwise_identical():
+    inp = mi.make_inputs(dtype="bf16", seqlens=[700, 33], num_heads=8, num_kv_heads=8,
+                         head_dim_nope=128, v_dim=128, causal=True, seed=4)
+    t = device_tensors(inp)
+    o1, l1 = run_gpu(inp, tensors=t)
+    o2, l2 = run_gpu(inp, tensors=t)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_all_sequences_empty_and_zero_max_seqlen():
+    from head_attention_forward_fa_amd import mha_fwd
+    dev = "cuda:0"
+    q = torch.zeros(0, 2, 128, dtype=torch.bfloat16, device=dev)
+    cu = torch.zeros(3, dtype=torch.int32, device=dev)
+    o, lse = mha_fwd(q, q, q, cu_seqlens=cu, max_seqlen=0, causal=True)
+    torch.cuda.synchronize()
+    assert o.shape == (0, 2, 128) and lse.shape == (2, 0)
+
+
+def test_overflowing_lengths_are_refused_without_writes():
+    # max_seqlen 128 sizes the table for one tile per (sequence, head); a
+    # 300-token sequence needs three, so the device refuses and writes nothing
+    from head_attention_forward_fa_amd import mha_fwd
+    inp = mi.make_inputs(dtype="bf16", seqlens=[300], num_heads=2, num_kv_heads=2,
+                         head_dim_nope=128, v_dim=128, causal=True, seed=5)
+    t = device_tensors(inp)
+    out = torch.full((300, 2, 128), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.full((2, 300), 7.0, dtype=torch.float32, device="cuda:0")
+    mha_fwd(t["q"], t["k"], t["v"], causal=True, cu_seqlens=t["cu_seqlens"], max_seqlen=128,
+            out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()) and bool((lse == 7.0).all())
+
+
+@pytest.mark.parametrize("block_m", [64, 128])
+@pytest.mark.parametrize("grid", [0, 1, 7, 1000])
+def test_scheduler_visits_every_item_once(block_m, grid):
+    from head_attention_forward_fa_amd import mha_sched_visit
+    rng = np.random.default_rng(block_m + grid)
+    lens = rng.integers(0, 1500, size=23)
+    lens[3] = 0
+    lens[5] = 1
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    hq, hkv = 8, 2
+    mx = int(lens.max())
+    visits = mha_sched_visit(torch.from_numpy(cu).cuda(), mx, hq, hkv, True, block_m, grid)
+    torch.cuda.synchronize()
+    tiles = (mx + block_m - 1) // block_m
+    want = np.zeros((hq, len(lens), tiles), dtype=np.int32)
+    for b, L in enumerate(lens):
+        want[:, b, : (L + block_m - 1) // block_m] = 1
+    assert np.array_equal(visits.cpu().numpy(), want)
+
+
+def test_scheduler_many_groups_index_mode():
+    # more (sequence, KV head) groups than the prepass ranks in LDS: the
+    # contiguous-range queue assignment must still cover every item once
+    from head_attention_forward_fa_amd import mha_sched_visit
+    rng = np.random.default_rng(9)
+    lens = rng.integers(0, 300, size=700)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    hq, hkv = 8, 4
+    mx = int(lens.max())
+    visits = mha_sched_visit(torch.from_numpy(cu).cuda(), mx, hq, hkv, False, 128, 0)
+    torch.cuda.synchronize()
+    tiles = (mx + 127) // 128
+    want = np.zeros((hq, len(lens), tiles), dtype=np.int32)
+    for b, L in enumerate(lens):
+        want[:, b, : (L + 127) // 128] = 1
+    assert np.array_equal(visits.cpu().numpy(), want)
