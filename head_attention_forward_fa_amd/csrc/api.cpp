@@ -115,9 +115,8 @@ int make_plan(int batch, int max_seqlen, int num_heads, int num_kv_heads, int bl
   return MHA_OK;
 }
 
-int check_common(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
-                 int32_t num_heads, int32_t num_kv_heads) {
-  if (!cu_seqlens) return fail(MHA_ERR_INVALID_ARG, "cu_seqlens is NULL");
+int check_scalars(int32_t batch, int32_t max_seqlen, int32_t num_heads,
+                  int32_t num_kv_heads) {
   if (batch < 1) return fail(MHA_ERR_INVALID_ARG, "batch must be >= 1");
   if (max_seqlen < 0) return fail(MHA_ERR_INVALID_ARG, "max_seqlen must be >= 0");
   if (num_heads < 1 || num_kv_heads < 1)
@@ -145,26 +144,29 @@ int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
             const void* q_rope, const void* k_rope, int32_t causal, float softmax_scale,
             int32_t dtype, const float* q_scale, const float* k_scale, void* stream) {
   g_err.clear();
-  if (!q || !k || !v || !o || !lse) return fail(MHA_ERR_INVALID_ARG, "q, k, v, o, lse must be non-NULL");
-  int rc = check_common(cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads);
+  int rc = check_scalars(batch, max_seqlen, num_heads, num_kv_heads);
   if (rc) return rc;
   if (head_dim_nope < 1 || head_dim_rope < 0 || v_dim < 1)
     return fail(MHA_ERR_INVALID_ARG, "head dims must be positive (rope >= 0)");
-  if ((q_rope == nullptr) != (k_rope == nullptr))
-    return fail(MHA_ERR_INVALID_ARG, "q_rope and k_rope must both be given or both NULL");
-  if ((head_dim_rope > 0) != (q_rope != nullptr))
-    return fail(MHA_ERR_INVALID_ARG, "rope pointers must be given iff head_dim_rope > 0");
   if (causal != 0 && causal != 1) return fail(MHA_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (dtype != MHA_DTYPE_F32 && dtype != MHA_DTYPE_BF16 && dtype != MHA_DTYPE_FP8_E4M3)
     return fail(MHA_ERR_INVALID_ARG, "unknown dtype");
-  const bool fp8 = dtype == MHA_DTYPE_FP8_E4M3;
-  if (fp8 != (q_scale != nullptr) || fp8 != (k_scale != nullptr))
-    return fail(MHA_ERR_INVALID_ARG, "q_scale and k_scale must be given iff dtype is FP8_E4M3");
   if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
     return fail(MHA_ERR_INVALID_ARG, "softmax_scale must be finite");
   const mha::Variant* var = mha::find_variant(dtype, head_dim_nope, head_dim_rope, v_dim);
   if (!var) return fail(MHA_ERR_UNSUPPORTED, "no compiled kernel for this (dtype, Dn, Dr, Dv)");
+  // every sequence empty: nothing is read, written or launched (empty
+  // tensors may come with NULL data pointers)
   if (max_seqlen == 0) return MHA_OK;
+  if (!q || !k || !v || !o || !lse || !cu_seqlens)
+    return fail(MHA_ERR_INVALID_ARG, "q, k, v, o, lse, cu_seqlens must be non-NULL");
+  if ((q_rope == nullptr) != (k_rope == nullptr))
+    return fail(MHA_ERR_INVALID_ARG, "q_rope and k_rope must both be given or both NULL");
+  if ((head_dim_rope > 0) != (q_rope != nullptr))
+    return fail(MHA_ERR_INVALID_ARG, "rope pointers must be given iff head_dim_rope > 0");
+  const bool fp8 = dtype == MHA_DTYPE_FP8_E4M3;
+  if (fp8 != (q_scale != nullptr) || fp8 != (k_scale != nullptr))
+    return fail(MHA_ERR_INVALID_ARG, "q_scale and k_scale must be given iff dtype is FP8_E4M3");
 
   Plan plan;
   rc = make_plan(batch, max_seqlen, num_heads, num_kv_heads, var->block_m, &plan);
@@ -219,8 +221,9 @@ int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen
                     int32_t num_heads, int32_t num_kv_heads, int32_t causal, int32_t block_m,
                     int32_t grid, int32_t* visits, void* stream) {
   g_err.clear();
-  int rc = check_common(cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads);
+  int rc = check_scalars(batch, max_seqlen, num_heads, num_kv_heads);
   if (rc) return rc;
+  if (!cu_seqlens) return fail(MHA_ERR_INVALID_ARG, "cu_seqlens is NULL");
   if (!visits) return fail(MHA_ERR_INVALID_ARG, "visits is NULL");
   if (causal != 0 && causal != 1) return fail(MHA_ERR_INVALID_ARG, "causal must be 0 or 1");
   int block_n;

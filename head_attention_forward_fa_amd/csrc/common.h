@@ -67,14 +67,29 @@ struct AttnParams {
   float scale_log2;   // sigma * log2(e)
 };
 
-// round-to-nearest-even float -> bf16 bits (inputs are finite here)
-__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even
+// (one v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
+  bf16x2 r = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// acc + a.lo + a.hi for a packed bf16 pair (v_dot2_f32_bf16 against 1.0).
+__device__ __forceinline__ float add_bf16x2(uint32_t a, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), one, acc, false);
+}
+
+// Buffer resource over [base, base + bytes): loads at offsets past the end
+// return zeros, with no branch (raw buffer, stride 0; gfx9 dword3 config).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
 // Combine a value across the two 32-lane halves of the wave (lanes i and

@@ -76,7 +76,9 @@ typedef enum {
  *   batch       number of sequences, >= 1
  *   max_seqlen  >= every sequence length; sizes the work table (num_heads *
  *               batch * ceil(max_seqlen / 128) entries).  0 means every
- *               sequence is empty: nothing is launched.  When the lengths
+ *               sequence is empty: the scalar arguments are still checked,
+ *               but nothing is read, written or launched and the tensor
+ *               pointers may be NULL.  When the lengths
  *               break this bound so far that the work items would not fit in
  *               that table, the device refuses the whole call and writes
  *               nothing.
