@@ -109,6 +109,9 @@ def main(argv=None):
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=mi.WORKLOAD_ORDER)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (five "
+                         "times), to calibrate HBM byte counters against a known size")
     a = ap.parse_args(argv)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): this path has no "
@@ -122,6 +125,16 @@ def main(argv=None):
     _native.load()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.copy_probe_mib:
+        n = a.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copied {a.copy_probe_mib} MiB five times", file=sys.stderr)
+        return 0
     inp = mi.workload(a.workload)
     print(f"[bench] workload {inp.name}: T={inp.total_tokens} Hq={inp.num_heads} "
           f"Hkv={inp.num_kv_heads} D={inp.head_dim_nope}+{inp.head_dim_rope}/{inp.v_dim}",

@@ -21,7 +21,8 @@ MHA_ERR_INVALID_ARG = 1
 MHA_ERR_UNSUPPORTED = 2
 MHA_ERR_HIP = 3
 
-EXPORTS = ("mha_fwd", "mha_fwd_last_error", "mha_fwd_supported", "mha_sched_visit")
+EXPORTS = ("mha_fwd", "mha_fwd_last_error", "mha_fwd_supported", "mha_fwd_kernel_info",
+           "mha_sched_visit")
 
 _lib = None
 
@@ -55,6 +56,9 @@ def load() -> ctypes.CDLL:
     lib.mha_fwd_last_error.restype = ctypes.c_char_p
     lib.mha_fwd_supported.argtypes = [i32, i32, i32, i32]
     lib.mha_fwd_supported.restype = ctypes.c_int
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.mha_fwd_kernel_info.argtypes = [i32, i32, i32, i32, ip, ip, ip, ip]
+    lib.mha_fwd_kernel_info.restype = ctypes.c_int
     lib.mha_sched_visit.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.mha_sched_visit.restype = ctypes.c_int
     _lib = lib

@@ -217,6 +217,23 @@ int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   return MHA_OK;
 }
 
+int mha_fwd_kernel_info(int32_t dtype, int32_t head_dim_nope, int32_t head_dim_rope,
+                        int32_t v_dim, int32_t* block_m, int32_t* blocks_per_cu, int32_t* grid,
+                        int32_t* lds_bytes) {
+  g_err.clear();
+  const mha::Variant* var = mha::find_variant(dtype, head_dim_nope, head_dim_rope, v_dim);
+  if (!var) return fail(MHA_ERR_UNSUPPORTED, "no compiled kernel for this (dtype, Dn, Dr, Dv)");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  const int bpc = var->blocks_per_cu();
+  if (block_m) *block_m = var->block_m;
+  if (blocks_per_cu) *blocks_per_cu = bpc;
+  if (grid) *grid = cu_count(dev) * bpc;
+  if (lds_bytes) *lds_bytes = var->lds_bytes;
+  return MHA_OK;
+}
+
 int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
                     int32_t num_heads, int32_t num_kv_heads, int32_t causal, int32_t block_m,
                     int32_t grid, int32_t* visits, void* stream) {

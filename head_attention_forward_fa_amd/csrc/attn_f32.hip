@@ -156,9 +156,9 @@ int blocks_f32() {
 }
 
 const Variant kF32[] = {
-    {launch_f32<64, 0, 64>, blocks_f32<64, 0, 64>, BM, BN},
-    {launch_f32<128, 0, 128>, blocks_f32<128, 0, 128>, BM, BN},
-    {launch_f32<128, 64, 128>, blocks_f32<128, 64, 128>, BM, BN},
+    {launch_f32<64, 0, 64>, blocks_f32<64, 0, 64>, BM, BN, (int)sizeof(float) * BN * (64+0+64)},
+    {launch_f32<128, 0, 128>, blocks_f32<128, 0, 128>, BM, BN, (int)sizeof(float) * BN * (128+0+128)},
+    {launch_f32<128, 64, 128>, blocks_f32<128, 64, 128>, BM, BN, (int)sizeof(float) * BN * (128+64+128)},
 };
 
 }  // namespace

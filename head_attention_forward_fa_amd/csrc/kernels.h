@@ -30,6 +30,7 @@ struct Variant {
   int (*blocks_per_cu)();
   int block_m;
   int block_n;
+  int lds_bytes;
 };
 
 // Lookup of the compiled variant for (dtype, Dn, Dr, Dv); nullptr if none.

@@ -50,33 +50,31 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
     int bm, int bn, int capacity, int2* __restrict__ table, SchedState* __restrict__ st,
     int* __restrict__ scratch) {
   __shared__ long long s_cost[kSortedMax];
-  __shared__ int s_items[kSortedMax];
-  __shared__ int s_order[kSortedMax];   // rank -> group
-  __shared__ int s_bin[kSortedMax];     // group -> queue
-  __shared__ int s_off[kSortedMax];     // group -> offset inside its queue
+  __shared__ int s_items[kSortedMax];   // group -> item count
+  __shared__ int s_irank[kSortedMax];   // rank -> item count
+  __shared__ int s_grank[kSortedMax];   // group -> rank
+  __shared__ int s_off[kSortedMax];     // rank -> offset inside its queue
   __shared__ int s_fill[kNumXcd];
-  __shared__ unsigned long long s_total;  // 64-bit: garbage lengths must not wrap
+  __shared__ int s_base[kNumXcd];
   __shared__ int s_bad;
 
   const int tid = threadIdx.x;
   const int group = num_heads / num_kv_heads;
   const int n = batch * num_kv_heads;
   const bool sorted = n <= kSortedMax;
-  if (tid == 0) {
-    s_total = 0ull;
-    s_bad = 0;
-  }
-  if (tid < kNumXcd) s_fill[tid] = 0;
+  if (tid == 0) s_bad = 0;
   __syncthreads();
 
-  // A: per-group cost and item count
+  // A: per-group cost and item count; the item total by a block reduction
+  // (in 64 bits: garbage lengths must not wrap past the capacity check)
+  long long my_items = 0;
   for (int i = tid; i < n; i += kPrepassThreads) {
-    int b = i / num_kv_heads;
-    int L = cu[b + 1] - cu[b];
-    int nqt = L > 0 ? (L + bm - 1) / bm : 0;
-    if (L < 0 || nqt >= kMaxQTilesPerSeq) atomicOr(&s_bad, 1);
-    int items = nqt * group;
-    atomicAdd(&s_total, (unsigned long long)items);
+    const int b = i / num_kv_heads;
+    const int L = cu[b + 1] - cu[b];
+    const int nqt = L > 0 ? (L + bm - 1) / bm : 0;
+    if (L < 0 || nqt >= kMaxQTilesPerSeq) s_bad = 1;
+    const int items = nqt * group;
+    my_items += items;
     if (sorted) {
       s_cost[i] = group_cost(L, bm, bn, causal) * group;
       s_items[i] = items;
@@ -84,8 +82,13 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
       scratch[i] = items;
     }
   }
+  for (int d = kWave / 2; d > 0; d >>= 1) my_items += __shfl_down(my_items, d);
+  __shared__ long long s_wsum[kPrepassThreads / kWave];
+  if ((tid & (kWave - 1)) == 0) s_wsum[tid / kWave] = my_items;
   __syncthreads();
-  if (s_bad || s_total > (unsigned long long)capacity) {
+  long long total = 0;
+  for (int w = 0; w < kPrepassThreads / kWave; ++w) total += s_wsum[w];
+  if (s_bad || total > (long long)capacity) {
     if (tid < kNumXcd) {
       st->counters[tid] = 0;
       st->base[tid] = 0;
@@ -99,26 +102,36 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
   }
 
   if (sorted) {
-    // B: rank groups by cost, largest first (ties by index), snake-deal to queues
+    // B: rank groups by cost, largest first (ties by index)
     for (int i = tid; i < n; i += kPrepassThreads) {
-      long long c = s_cost[i];
+      const long long c = s_cost[i];
       int rank = 0;
+#pragma unroll 8
       for (int j = 0; j < n; ++j) {
-        long long cj = s_cost[j];
+        const long long cj = s_cost[j];
         rank += (cj > c) || (cj == c && j < i);
       }
-      s_order[rank] = i;
+      s_grank[i] = rank;
+      s_irank[rank] = s_items[i];
     }
     __syncthreads();
-    for (int r = tid; r < n; r += kPrepassThreads) {
-      int bin = snake_bin(r);
+    // C: snake-deal ranks to queues (rank r -> queue snake_bin(r)); queue x
+    // holds ranks x, 15-x, 16+x, 31-x, ...  One thread per queue walks its
+    // ranks in order and lays them out back to back.
+    if (tid < kNumXcd) {
       int off = 0;
-      for (int r2 = bin; r2 < r; ++r2)
-        if (snake_bin(r2) == bin) off += s_items[s_order[r2]];
-      int g = s_order[r];
-      s_bin[g] = bin;
-      s_off[g] = off;
-      atomicAdd(&s_fill[bin], s_items[g]);
+      for (int r0 = 0; r0 < n; r0 += 2 * kNumXcd) {
+        const int ra = r0 + tid, rb = r0 + 2 * kNumXcd - 1 - tid;
+        if (ra < n) {
+          s_off[ra] = off;
+          off += s_irank[ra];
+        }
+        if (rb < n) {
+          s_off[rb] = off;
+          off += s_irank[rb];
+        }
+      }
+      s_fill[tid] = off;
     }
     __syncthreads();
   } else {
@@ -129,12 +142,12 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
     if (tid == 0) s_carry = 0;
     __syncthreads();
     for (int c0 = 0; c0 < n; c0 += kPrepassThreads) {
-      int i = c0 + tid;
-      int v = i < n ? scratch[i] : 0;
+      const int i = c0 + tid;
+      const int v = i < n ? scratch[i] : 0;
       s_scan[tid] = v;
       __syncthreads();
       for (int d = 1; d < kPrepassThreads; d <<= 1) {
-        int add = tid >= d ? s_scan[tid - d] : 0;
+        const int add = tid >= d ? s_scan[tid - d] : 0;
         __syncthreads();
         s_scan[tid] += add;
         __syncthreads();
@@ -144,42 +157,41 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
       if (tid == kPrepassThreads - 1) s_carry += s_scan[tid];
       __syncthreads();
     }
+    if (tid < kNumXcd) {
+      const int lo = (int)((long long)tid * n / kNumXcd);
+      const int hi = (int)((long long)(tid + 1) * n / kNumXcd);
+      const int plo = lo < n ? scratch[lo] : (int)total;
+      const int phi = hi < n ? scratch[hi] : (int)total;
+      s_fill[tid] = phi - plo;
+    }
+    __syncthreads();
   }
 
-  // C: queue slices
+  // D: queue slices
   if (tid == 0) {
     int base = 0;
     for (int x = 0; x < kNumXcd; ++x) {
-      int cnt;
-      if (sorted) {
-        cnt = s_fill[x];
-      } else {
-        int lo = (int)((long long)x * n / kNumXcd), hi = (int)((long long)(x + 1) * n / kNumXcd);
-        int plo = lo < n ? scratch[lo] : (int)s_total;
-        int phi = hi < n ? scratch[hi] : (int)s_total;
-        cnt = phi - plo;
-      }
+      s_base[x] = base;
       st->base[x] = base;
-      st->count[x] = cnt;
+      st->count[x] = s_fill[x];
       st->counters[x] = 0;
-      base += cnt;
+      base += s_fill[x];
     }
     st->status = 0;
-    st->total = (int)s_total;
+    st->total = (int)total;
   }
   __syncthreads();
 
-  // D: write the items of each group, q-tiles longest first, heads inner
+  // E: write the items of each group, q-tiles longest first, heads inner
   for (int i = tid; i < n; i += kPrepassThreads) {
-    int b = i / num_kv_heads;
-    int g = i % num_kv_heads;
-    int L = cu[b + 1] - cu[b];
-    int nqt = L > 0 ? (L + bm - 1) / bm : 0;
+    const int b = i / num_kv_heads;
+    const int g = i % num_kv_heads;
+    const int L = cu[b + 1] - cu[b];
+    const int nqt = L > 0 ? (L + bm - 1) / bm : 0;
     int pos;
     if (sorted) {
-      int base = 0;
-      for (int x = 0; x < s_bin[i]; ++x) base += s_fill[x];
-      pos = base + s_off[i];
+      const int r = s_grank[i];
+      pos = s_base[snake_bin(r)] + s_off[r];
     } else {
       pos = scratch[i];  // queues are contiguous in index order
     }

@@ -117,6 +117,17 @@ def mha_fwd_supported(dtype_code: int, head_dim_nope: int, head_dim_rope: int, v
     return bool(nat.load().mha_fwd_supported(dtype_code, head_dim_nope, head_dim_rope, v_dim))
 
 
+def mha_fwd_kernel_info(dtype_code: int, head_dim_nope: int, head_dim_rope: int,
+                        v_dim: int) -> dict:
+    """Launch facts of the kernel mha_fwd uses for this shape on the current device."""
+    import ctypes
+    vals = [ctypes.c_int32(0) for _ in range(4)]
+    st = nat.load().mha_fwd_kernel_info(dtype_code, head_dim_nope, head_dim_rope, v_dim,
+                                        *[ctypes.byref(v) for v in vals])
+    nat.check(st)
+    return dict(zip(("block_m", "blocks_per_cu", "grid", "lds_bytes"), (v.value for v in vals)))
+
+
 def mha_sched_visit(cu_seqlens: torch.Tensor, max_seqlen: int, num_heads: int,
                     num_kv_heads: int, causal: bool, block_m: int = 128,
                     grid: int = 0) -> torch.Tensor:

@@ -75,7 +75,8 @@ typedef enum {
  *               (that would need a device sync).
  *   batch       number of sequences, >= 1
  *   max_seqlen  >= every sequence length; sizes the work table (num_heads *
- *               batch * ceil(max_seqlen / 128) entries).  0 means every
+ *               batch * ceil(max_seqlen / block_m) entries, block_m = 64
+ *               for float32 and 128 for bf16 / fp8).  0 means every
  *               sequence is empty: the scalar arguments are still checked,
  *               but nothing is read, written or launched and the tensor
  *               pointers may be NULL.  When the lengths
@@ -127,6 +128,19 @@ const char* mha_fwd_last_error(void);
 /* 1 if (dtype, Dn, Dr, Dv) is in the compiled set, else 0.  No HIP call. */
 int mha_fwd_supported(int32_t dtype, int32_t head_dim_nope,
                       int32_t head_dim_rope, int32_t v_dim);
+
+/*
+ * mha_fwd_kernel_info -- launch facts of the kernel that mha_fwd would use for
+ * (dtype, Dn, Dr, Dv) on the current device: *block_m = query rows per work
+ * item, *blocks_per_cu = workgroups resident per compute unit (its register
+ * and LDS footprint allow), *grid = workgroups of the persistent launch
+ * before clamping to the number of work items, *lds_bytes = static LDS per
+ * workgroup.  Any output pointer may be NULL.  Returns MHA_ERR_UNSUPPORTED
+ * outside the compiled set, MHA_ERR_HIP if the device cannot be queried.
+ */
+int mha_fwd_kernel_info(int32_t dtype, int32_t head_dim_nope, int32_t head_dim_rope,
+                        int32_t v_dim, int32_t* block_m, int32_t* blocks_per_cu,
+                        int32_t* grid, int32_t* lds_bytes);
 
 /*
  * mha_sched_visit -- diagnostic for the persistent tile scheduler
