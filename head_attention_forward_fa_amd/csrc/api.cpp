@@ -44,7 +44,7 @@ int fail_hip(hipError_t e, const char* what) {
   return MHA_ERR_HIP;
 }
 
-// Scheduler workspace: [SchedState | table (int2 x capacity) | scratch (int x groups)]
+// Scheduler workspace: [SchedState | table (16-byte entries x capacity) | scratch (int x groups)]
 struct Workspace {
   char* buf = nullptr;
   size_t bytes = 0;
@@ -53,7 +53,8 @@ struct Workspace {
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Workspace> g_ws;
 
-constexpr size_t kStateBytes = 256;
+constexpr size_t kStateBytes = (sizeof(mha::SchedState) + 255) / 256 * 256;
+static_assert(alignof(mha::SchedState) <= 256, "workspace base is 256-byte aligned");
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -110,7 +111,7 @@ int make_plan(int batch, int max_seqlen, int num_heads, int num_kv_heads, int bl
   if (groups > INT_MAX / 2) return fail(MHA_ERR_INVALID_ARG, "batch * num_kv_heads too large");
   plan->capacity = (int)cap;
   plan->groups = (int)groups;
-  plan->bytes = kStateBytes + align_up((size_t)cap * sizeof(int2), 256) +
+  plan->bytes = kStateBytes + align_up((size_t)cap * sizeof(mha::i32x4), 256) +
                 align_up((size_t)groups * sizeof(int), 256);
   return MHA_OK;
 }
@@ -182,8 +183,8 @@ int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   e = get_workspace(dev, s, plan.bytes, &ws);
   if (e != hipSuccess) return fail_hip(e, "workspace allocation");
   auto* st = reinterpret_cast<mha::SchedState*>(ws);
-  auto* table = reinterpret_cast<int2*>(ws + kStateBytes);
-  auto* scratch = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(int2), 256));
+  auto* table = reinterpret_cast<mha::i32x4*>(ws + kStateBytes);
+  auto* scratch = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
 
   e = mha::launch_prepass(cu_seqlens, batch, num_heads, num_kv_heads, causal, var->block_m,
                           var->block_n, plan.capacity, table, st, scratch, s);
@@ -263,14 +264,14 @@ int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen
   e = get_workspace(dev, s, plan.bytes, &ws);
   if (e != hipSuccess) return fail_hip(e, "workspace allocation");
   auto* st = reinterpret_cast<mha::SchedState*>(ws);
-  auto* table = reinterpret_cast<int2*>(ws + kStateBytes);
-  auto* scratch = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(int2), 256));
+  auto* table = reinterpret_cast<mha::i32x4*>(ws + kStateBytes);
+  auto* scratch = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
   e = mha::launch_prepass(cu_seqlens, batch, num_heads, num_kv_heads, causal, block_m, block_n,
                           plan.capacity, table, st, scratch, s);
   if (e != hipSuccess) return fail_hip(e, "scheduler prepass launch");
   if (grid == 0) grid = cu_count(dev) * 2;
   const int tiles = (int)(((long long)max_seqlen + block_m - 1) / block_m);
-  e = mha::launch_sched_visit(cu_seqlens, batch, num_heads, tiles, table, st, visits, grid, s);
+  e = mha::launch_sched_visit(batch, num_heads, tiles, table, st, visits, grid, s);
   if (e != hipSuccess) return fail_hip(e, "visit kernel launch");
   return MHA_OK;
 }

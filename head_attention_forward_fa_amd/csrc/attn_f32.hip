@@ -26,7 +26,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
 
   __shared__ float s_k[BN][DQK];
   __shared__ float s_v[BN][DV];
-  __shared__ int2 s_slot[2];
+  __shared__ i32x4 s_item[2];
 
   const int tid = threadIdx.x;
   const int sub = tid & 3;
@@ -39,18 +39,23 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
   float* __restrict__ o = static_cast<float*>(p.o);
   const int T = p.cu_seqlens[p.batch];
 
-  int queue = blockIdx.x % kNumXcd, tried = 0;
+  // wave 0 runs the work-item source; the next item's entry is published at
+  // the end of the current item
+  Fetcher fetch;
+  const bool w0 = __builtin_amdgcn_readfirstlane(tid >> 6) == 0;
+  if (w0) {
+    fetch.init(p.sched);
+    const i32x4 e0 = fetch.take(p.sched, p.table);
+    if (tid == 0) s_item[0] = e0;
+  }
   for (int it = 0;; ++it) {
-    if (tid == 0) {
-      int2 e;
-      s_slot[it & 1] = fetch_item(p.sched, p.table, queue, tried, e) ? e : make_int2(-1, 0);
-    }
     __syncthreads();
-    const int2 e = s_slot[it & 1];
-    if (e.x < 0) break;
-    const WorkItem w = decode_item(e);
-    const int s0 = p.cu_seqlens[w.b];
-    const int L = p.cu_seqlens[w.b + 1] - s0;
+    const WorkItem w = decode_item(s_item[it & 1]);
+    if (w.L < 0) break;
+    i32x4 nxt;
+    if (w0) nxt = fetch.take(p.sched, p.table);
+    const int s0 = w.s0;
+    const int L = w.L;
     const int g = w.h / p.group;
     const int qi = w.qt * BM + row;  // query row inside the sequence
     const bool qvalid = qi < L;
@@ -134,6 +139,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
       if (sub == 0)
         p.lse[(size_t)w.h * T + s0 + qi] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
     }
+    if (tid == 0) s_item[(it + 1) & 1] = nxt;
   }
 }
 

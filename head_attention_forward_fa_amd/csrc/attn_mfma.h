@@ -468,7 +468,7 @@ struct MfmaKernel {
   // ------------------------------------------------------------ kernel body
 
   static __device__ void run(const AttnParams& p, char* smem) {
-    __shared__ int2 s_slot[2];
+    __shared__ i32x4 s_item[2];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int lane32 = lane & 31;
@@ -479,20 +479,27 @@ struct MfmaKernel {
     const char* __restrict__ qrp = static_cast<const char*>(p.q_rope);
     char* __restrict__ op = static_cast<char*>(p.o);
 
-    int queue = blockIdx.x % kNumXcd, tried = 0;
+    // wave 0 runs the work-item source; the next item's table entry is read
+    // while the current item's first blocks load and published at the first
+    // barrier after that
+    Fetcher fetch;
+    if (wave == 0) {
+      fetch.init(p.sched);
+      const i32x4 e0 = fetch.take(p.sched, p.table);
+      if (tid == 0) s_item[0] = e0;
+    }
     for (int it = 0;; ++it) {
-      if (tid == 0) {
-        int2 e;
-        s_slot[it & 1] = fetch_item(p.sched, p.table, queue, tried, e) ? e : make_int2(-1, 0);
-      }
       __syncthreads();
       // the item is the same for the whole workgroup: keep it in SGPRs
-      const int2 e = make_int2(__builtin_amdgcn_readfirstlane(s_slot[it & 1].x),
-                               __builtin_amdgcn_readfirstlane(s_slot[it & 1].y));
-      if (e.x < 0) break;
-      const WorkItem wi = decode_item(e);
-      const int s0 = __builtin_amdgcn_readfirstlane(p.cu_seqlens[wi.b]);
-      const int L = __builtin_amdgcn_readfirstlane(p.cu_seqlens[wi.b + 1]) - s0;
+      const WorkItem wi = decode_item(i32x4{__builtin_amdgcn_readfirstlane(s_item[it & 1][0]),
+                                            __builtin_amdgcn_readfirstlane(s_item[it & 1][1]),
+                                            __builtin_amdgcn_readfirstlane(s_item[it & 1][2]),
+                                            __builtin_amdgcn_readfirstlane(s_item[it & 1][3])});
+      if (wi.L < 0) break;
+      i32x4 nxt;
+      if (wave == 0) nxt = fetch.take(p.sched, p.table);
+      const int s0 = wi.s0;
+      const int L = wi.L;
       const int g = wi.h / p.group;
       const int q0 = wi.qt * C::BM;    // first query row of the tile
       const int wq0 = q0 + wave * 32;  // first query row of this wave
@@ -552,8 +559,10 @@ struct MfmaKernel {
       w.m = -INFINITY;
       w.l = 0.f;
 
-      // prologue: block 0's K and V land; S_0; K_1 lands
+      // prologue: block 0's K and V (and the next item's entry) land; S_0;
+      // K_1 lands
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
+      if (tid == 0) s_item[(it + 1) & 1] = nxt;
       __syncthreads();
       s_block(smem, qf, lane32, hf, cq, w);
       if (nblocks > 1) load_k(p, smem + C::KSLOT, wave, lane, s0, L, g, C::BN);

@@ -20,28 +20,35 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-// A work item of the persistent scheduler: sequence b, query head h, query
-// tile qt.  Packed as {b, (h << 20) | qt}.
+// A work item of the persistent scheduler: query tile qt of query head h
+// over sequence b, whose tokens are s0 .. s0 + L - 1.  A table entry is the
+// 16-byte vector {s0, L, (h << 20) | qt, b}; L = -1 marks "no work left".
 struct WorkItem {
-  int b, h, qt;
+  int s0, L, h, qt, b;
 };
-__device__ __forceinline__ WorkItem decode_item(int2 e) {
-  return WorkItem{e.x, (int)((unsigned)e.y >> 20), e.y & 0xFFFFF};
+__device__ __forceinline__ WorkItem decode_item(const i32x4& e) {
+  return WorkItem{e[0], e[1], (int)((unsigned)e[2] >> 20), e[2] & 0xFFFFF, e[3]};
 }
 constexpr int kMaxQTilesPerSeq = 1 << 20;
 constexpr int kMaxHeads = 1 << 11;
 
-// Scheduler state kept in device memory (the library workspace).
-//   counters[x]  next index to hand out from queue x (one queue per XCD)
-//   base[x], count[x]  queue x's slice of the work table
+// Scheduler state kept in device memory (the library workspace).  Each
+// queue (one per XCD) sits on its own 256-byte line, so that the atomic
+// adds of different queues never meet on one cache line.
+//   counter      next index to hand out from the queue
+//   base, count  the queue's slice of the work table
 //   status       nonzero when the prepass refused the problem
+struct alignas(256) SchedQueue {
+  int counter;
+  int base;
+  int count;
+  int pad[61];
+};
 struct SchedState {
-  int counters[kNumXcd];
-  int base[kNumXcd];
-  int count[kNumXcd];
+  SchedQueue q[kNumXcd];
   int status;
   int total;
-  int pad[6];
+  int pad[62];
 };
 
 // Kernel parameters (one struct so the launch signature stays the same for
@@ -57,7 +64,7 @@ struct AttnParams {
   const float* q_scale;
   const float* k_scale;
   const int32_t* cu_seqlens;
-  const int2* table;
+  const i32x4* table;
   SchedState* sched;
   int batch;
   int num_heads;
@@ -113,25 +120,49 @@ __device__ __forceinline__ bool wave_any(bool p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Fetch the next work item for this workgroup.  Queue choice is XCD-aware:
-// workgroup i is dispatched to XCD i % 8, so it drains queue i % 8 first
-// (whose items share K/V and therefore that XCD's L2), then the others.
-// Called by one thread; returns false when every queue is empty.
-__device__ __forceinline__ bool fetch_item(SchedState* s, const int2* table, int& queue,
-                                           int& tried, int2& out) {
-  while (tried < kNumXcd) {
-    int cnt = s->count[queue];
-    if (cnt > 0) {
-      int idx = atomicAdd(&s->counters[queue], 1);
-      if (idx < cnt) {
-        out = table[s->base[queue] + idx];
-        return true;
-      }
-    }
-    queue = (queue + 1) % kNumXcd;
-    ++tried;
+// Work-item source of one workgroup, driven by one wave (all its lanes take
+// the same path; only lane 0 touches the counters).  Queue choice is
+// XCD-aware: workgroup i is dispatched to XCD i % 8, so it drains queue
+// i % 8 first (whose items share K/V and therefore that XCD's L2), then the
+// others.  The index of the following item is reserved (atomic add) one
+// item ahead and read back only at the next take(); take() itself only
+// issues the table read, whose value the caller needs later.  So neither
+// memory round trip has to sit between two items.
+struct Fetcher {
+  int queue, tried, cnt, base;  // wave-uniform
+  int pend;                     // lane 0: the reserved index (in flight until the next take)
+
+  __device__ __forceinline__ void open_queue(const SchedState* st) {
+    cnt = __builtin_amdgcn_readfirstlane(st->q[queue].count);
+    base = __builtin_amdgcn_readfirstlane(st->q[queue].base);
   }
-  return false;
-}
+  __device__ __forceinline__ void reserve(SchedState* st) {
+    pend = 0;
+    if (__lane_id() == 0) pend = atomicAdd(&st->q[queue].counter, 1);
+  }
+  __device__ __forceinline__ void init(SchedState* st) {
+    queue = blockIdx.x % kNumXcd;
+    tried = 0;
+    open_queue(st);
+    reserve(st);
+  }
+  // Entry of the reserved index (moving on to the next queue once this one
+  // is exhausted) and a reservation of the index after it; L = -1 when every
+  // queue is exhausted.
+  __device__ __forceinline__ i32x4 take(SchedState* st, const i32x4* table) {
+    for (;;) {
+      const int idx = __builtin_amdgcn_readfirstlane(pend);
+      if (idx < cnt) {
+        const i32x4 e = table[base + idx];
+        reserve(st);
+        return e;
+      }
+      if (++tried >= kNumXcd) return i32x4{0, -1, 0, 0};
+      queue = (queue + 1) % kNumXcd;
+      open_queue(st);
+      reserve(st);
+    }
+  }
+};
 
 }  // namespace mha

@@ -16,11 +16,11 @@ constexpr int kBlockM_F32 = 64;
 constexpr int kBlockN_F32 = 32;
 
 hipError_t launch_prepass(const int32_t* cu, int batch, int num_heads, int num_kv_heads,
-                          int causal, int bm, int bn, int capacity, int2* table,
+                          int causal, int bm, int bn, int capacity, i32x4* table,
                           SchedState* st, int* scratch, hipStream_t stream);
 
-hipError_t launch_sched_visit(const int32_t* cu, int batch, int num_heads, int tiles,
-                              const int2* table, SchedState* st, int* visits, int grid,
+hipError_t launch_sched_visit(int batch, int num_heads, int tiles, const i32x4* table,
+                              SchedState* st, int* visits, int grid,
                               hipStream_t stream);
 
 // A kernel variant: its launcher and its occupancy (resident workgroups per

@@ -1,21 +1,22 @@
 // Persistent tile scheduler: the prepass that builds the work table and the
 // diagnostic visit kernel.
 //
-// The pages describe the scheduler as a trait (MHATileScheduler: "maps work
-// tiles to thread blocks, advances the per-CTA state through the work grid
-// across kernel iterations, and reports the grid dimensions required for
-// launch"), generic over an optional pointer of per-batch sequence-length
-// offsets (Required methods: get_current_work_info, ValidLengthType), with
-// a shared-memory slot that publishes the active work index to the block
-// (initial_state) and an advance() that reports whether work remains.  The
-// MI355X version:
+// The pages give the scheduler as a trait (MHATileScheduler): it assigns
+// work tiles to thread blocks, steps each block's state through the work
+// across iterations of a persistent kernel, reports the launch grid, and is
+// generic over an optional pointer to per-batch sequence-length offsets
+// (Required methods: get_current_work_info, ValidLengthType); the active
+// work index is published to the block through shared memory
+// (initial_state), and advance() tells whether work remains.  The MI355X
+// version:
 //
 //   * a one-workgroup prepass turns cu_seqlens into a table of work items
-//     (b, h, q-tile).  Items are grouped by (sequence, KV head), so that the
-//     query heads sharing a KV head and every q-tile of that sequence sit
-//     next to each other; groups are dealt to 8 queues, one per XCD, largest
-//     first in a snake order so the queues carry equal work; inside a group
-//     the q-tiles run longest first (causal cost grows with the tile index).
+//     {s0, L, h, q-tile, b}.  Items are grouped by (sequence, KV head), so
+//     that the query heads sharing a KV head and every q-tile of that
+//     sequence sit next to each other; groups are dealt to 8 queues, one per
+//     XCD, largest first in a snake order so the queues carry equal work;
+//     inside a group the q-tiles run longest first (causal cost grows with
+//     the tile index).
 //   * the attention kernel is launched with about (CUs x resident
 //     workgroups) workgroups; each pops items from queue blockIdx % 8 with
 //     one atomic add, then helps the other queues once its own is empty.
@@ -47,7 +48,7 @@ __device__ __forceinline__ int snake_bin(int r) {
 
 __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
     const int32_t* __restrict__ cu, int batch, int num_heads, int num_kv_heads, int causal,
-    int bm, int bn, int capacity, int2* __restrict__ table, SchedState* __restrict__ st,
+    int bm, int bn, int capacity, i32x4* __restrict__ table, SchedState* __restrict__ st,
     int* __restrict__ scratch) {
   __shared__ long long s_cost[kSortedMax];
   __shared__ int s_items[kSortedMax];   // group -> item count
@@ -90,9 +91,9 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
   for (int w = 0; w < kPrepassThreads / kWave; ++w) total += s_wsum[w];
   if (s_bad || total > (long long)capacity) {
     if (tid < kNumXcd) {
-      st->counters[tid] = 0;
-      st->base[tid] = 0;
-      st->count[tid] = 0;
+      st->q[tid].counter = 0;
+      st->q[tid].base = 0;
+      st->q[tid].count = 0;
     }
     if (tid == 0) {
       st->status = 1;
@@ -172,9 +173,9 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
     int base = 0;
     for (int x = 0; x < kNumXcd; ++x) {
       s_base[x] = base;
-      st->base[x] = base;
-      st->count[x] = s_fill[x];
-      st->counters[x] = 0;
+      st->q[x].base = base;
+      st->q[x].count = s_fill[x];
+      st->q[x].counter = 0;
       base += s_fill[x];
     }
     st->status = 0;
@@ -186,7 +187,8 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
   for (int i = tid; i < n; i += kPrepassThreads) {
     const int b = i / num_kv_heads;
     const int g = i % num_kv_heads;
-    const int L = cu[b + 1] - cu[b];
+    const int s0 = cu[b];
+    const int L = cu[b + 1] - s0;
     const int nqt = L > 0 ? (L + bm - 1) / bm : 0;
     int pos;
     if (sorted) {
@@ -197,45 +199,51 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
     }
     for (int qt = nqt - 1; qt >= 0; --qt)
       for (int hh = 0; hh < group; ++hh)
-        table[pos++] = make_int2(b, ((g * group + hh) << 20) | qt);
+        table[pos++] = i32x4{s0, L, ((g * group + hh) << 20) | qt, b};
   }
 }
 
-__global__ __launch_bounds__(256) void sched_visit_kernel(const int32_t* __restrict__ cu,
-                                                           int batch, int num_heads, int tiles,
-                                                           const int2* __restrict__ table,
+__global__ __launch_bounds__(256) void sched_visit_kernel(int batch, int num_heads, int tiles,
+                                                           const i32x4* __restrict__ table,
                                                            SchedState* __restrict__ st,
                                                            int* __restrict__ visits) {
-  __shared__ int2 s_slot[2];
-  int queue = blockIdx.x % kNumXcd, tried = 0;
+  __shared__ i32x4 s_item[2];
+  Fetcher fetch;
+  const bool w0 = threadIdx.x < kWave;
+  if (w0) {
+    fetch.init(st);
+    const i32x4 e0 = fetch.take(st, table);
+    if (threadIdx.x == 0) s_item[0] = e0;
+  }
   for (int it = 0;; ++it) {
-    if (threadIdx.x == 0) {
-      int2 e;
-      s_slot[it & 1] = fetch_item(st, table, queue, tried, e) ? e : make_int2(-1, 0);
-    }
     __syncthreads();
-    int2 e = s_slot[it & 1];
-    if (e.x < 0) break;
-    WorkItem w = decode_item(e);
-    if (threadIdx.x == 0 && w.b < batch && w.h < num_heads && w.qt < tiles)
-      atomicAdd(&visits[(w.h * batch + w.b) * tiles + w.qt], 1);
+    const i32x4 e = s_item[it & 1];
+    if (e[1] < 0) break;
+    if (w0) {
+      const i32x4 nxt = fetch.take(st, table);
+      if (threadIdx.x == 0) {
+        s_item[(it + 1) & 1] = nxt;
+        const WorkItem w = decode_item(e);
+        if (w.b < batch && w.h < num_heads && w.qt < tiles)
+          atomicAdd(&visits[(w.h * batch + w.b) * tiles + w.qt], 1);
+      }
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_prepass(const int32_t* cu, int batch, int num_heads, int num_kv_heads,
-                          int causal, int bm, int bn, int capacity, int2* table,
+                          int causal, int bm, int bn, int capacity, i32x4* table,
                           SchedState* st, int* scratch, hipStream_t stream) {
   hipLaunchKernelGGL(sched_prepass_kernel, dim3(1), dim3(kPrepassThreads), 0, stream, cu, batch,
                      num_heads, num_kv_heads, causal, bm, bn, capacity, table, st, scratch);
   return hipGetLastError();
 }
 
-hipError_t launch_sched_visit(const int32_t* cu, int batch, int num_heads, int tiles,
-                              const int2* table, SchedState* st, int* visits, int grid,
-                              hipStream_t stream) {
-  hipLaunchKernelGGL(sched_visit_kernel, dim3(grid), dim3(256), 0, stream, cu, batch, num_heads,
+hipError_t launch_sched_visit(int batch, int num_heads, int tiles, const i32x4* table,
+                              SchedState* st, int* visits, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(sched_visit_kernel, dim3(grid), dim3(256), 0, stream, batch, num_heads,
                      tiles, table, st, visits);
   return hipGetLastError();
 }
