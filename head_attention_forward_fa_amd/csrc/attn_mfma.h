@@ -1,23 +1,28 @@
 // Matrix-core attention forward for bf16 and fp8 (E4M3) Q/K on gfx950.
 //
-// One work item = one (sequence, query head, 128-row query tile).  A
-// workgroup is 4 waves; wave w owns query rows 32w .. 32w+31 of the tile.
-// The tile of Q stays in registers for the whole item; K and V stream past
-// in 64-key blocks through LDS rings (the Q-stationary tiling with staged
-// K/V buffers of the pages: SM100AttentionSMem, comptime members q_bytes,
-// k_stage_bytes, v_stage_bytes; TMAProducerPipeline, acquire / commit_step).
+// One work item = one (sequence, query head, 256-row query tile).  A
+// workgroup is 8 waves (two per SIMD); wave w owns query rows 32w .. 32w+31
+// of the tile.  The tile of Q stays in registers for the whole item; K and V
+// stream past in 64-key blocks through LDS rings (the Q-stationary tiling
+// with staged K/V buffers of the pages: SM100AttentionSMem, comptime members
+// q_bytes, k_stage_bytes, v_stage_bytes; TMAProducerPipeline, acquire /
+// commit_step).
 //
 // Staging.  K (+ K_rope, + the fp8 k_scale) and V of coming blocks are
-// copied HBM -> LDS by buffer_load ... lds while the current block is
-// computed: each lane moves 16 bytes straight into LDS (lane i of an
-// instruction lands at byte 16 i of a 1 KiB run), with no register staging
-// and no VALU work.  The buffer resource of a block ends at the sequence's
-// last key, so rows past the end arrive as zeros.  Rows are stored as
-// 16-byte chunks in XOR-swizzled order (the global side picks which chunk
-// each lane fetches), so the matrix-core operand reads are free of LDS bank
-// conflicts.  The K ring runs one block ahead of the V ring.
+// copied HBM -> LDS by buffer_load ... lds: each lane moves 16 bytes straight
+// into LDS (lane i of an instruction lands at byte 16 i of a 1 KiB run), with
+// no register staging.  The K ring has 4 slots and the V ring 3, so block
+// j+3's K and block j+2's V are requested while block j is computed, two
+// blocks before they are needed; each wave spreads its few DMA instructions
+// over the matrix-core slots of the block's first step instead of issuing
+// them in one burst.  A block's buffer resource ends at the sequence's last
+// key, so rows past the end arrive as zeros.  K rows are stored at a pitch of
+// row + 16 bytes (consecutive rows start 4 banks apart, so the rows that one
+// operand read touches at a time fall on distinct banks, and every K operand
+// address is a per-lane base plus an immediate); V rows are unpadded, with
+// their 16-byte chunks in XOR-swizzled order for the transposed reads.
 //
-// Math per 64-key block j, per wave:
+// Math per 32-key sub-tile i, per wave:
 //   S^T = K Q^T on the matrix cores (v_mfma_f32_32x32x16_bf16, or for fp8
 //         v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales).  Keys run
 //         along the MFMA M axis and queries along N, so in the 32x32 output
@@ -27,29 +32,33 @@
 //   fp8:  S_ij *= k_scale_j, with q_scale_i folded into the exponent
 //         multiplier, after the product (per-token scales staged per tile:
 //         SM100AttentionSMem, Methods q_scale_smem, k_scale_smem).
-//   mask: only in blocks that cross the causal diagonal or the sequence end.
-//   online softmax in the log2 domain: m_i is the running row max of
+//   mask: only the wave's last sub-tile can cross the causal diagonal or the
+//         sequence end (sub-tiles and wave rows are both 32-aligned).
+//   online softmax in the log2 domain: m is the running row max of
 //         sigma*log2(e)*S; P = 2^(sigma*log2(e)*S - m) via v_exp_f32.  The
 //         correction of O and l (the per-row correction buffer of
 //         SM100AttentionSMem, Methods: correction_smem) is applied lazily,
 //         only when some row's max grows by more than 8 (a factor 256), so
-//         almost every block skips it; O and l always share the same stale m,
-//         so O / l and LSE = (m + log2 l) ln 2 are unchanged.
+//         almost every sub-tile skips it; O and l always share the same stale
+//         m, so O / l and LSE = (m + log2 l) ln 2 are unchanged.
 //   O^T += V^T P^T on the matrix cores.  P^T is already in the B-operand
 //         layout (lane = query, 8 k-slots), so it goes from the S registers to
 //         the PV product with one v_cvt_pk_bf16_f32 per pair.  V stays
 //         row-major in LDS ("mn-major" V of TMAProducerPipeline); the
 //         A-operand V^T fragments come from ds_read_b64_tr_b16.
 //
-// Schedule.  A 32x32x16 MFMA occupies the matrix pipe for ~32 cycles, of
-// which ~16-18 can overlap VALU work issued by the same wave (measured on
-// MI355X).  Each block is therefore written as two explicit software-
-// pipelined phases, slot by slot, with its operand read issued two slots
-// ahead:
-//   phase A  the S products of block j+1, each followed by a share of block
-//            j's exponentials, row sums and bf16 packing;
-//   phase B  block j's P V products, in the second half each followed by a
-//            share of block j+1's (fp8 k_scale and) row max.
+// Schedule.  Each sub-tile step is two software-pipelined phases, written
+// slot by slot with operand reads issued two slots ahead:
+//   phase A  the S products of sub-tile i+1 and sub-tile i's exponentials,
+//            row sums and bf16 packing;
+//   phase B  sub-tile i's P V products and sub-tile i+1's (fp8 k_scale and)
+//            row max.
+// The machine scheduler interleaves the independent vector work with the
+// matrix-core ops inside a step; the two waves that share a SIMD overlap
+// one's softmax with the other's products.
+// Pipelining at 32 keys keeps only two 32x32 S tiles live, which leaves the
+// registers for O, Q and the operand buffers within 256 VGPRs (two waves per
+// SIMD).  One barrier per 64-key block publishes the DMA'd slots.
 // Epilogue: O / l, bf16 round-to-nearest-even, staged through LDS for
 // coalesced 16-byte stores (the pages reuse the Q region for this,
 // SM100AttentionSMem Methods: o_smem), and LSE in natural log.
@@ -70,71 +79,80 @@ template <int DN_, int DR_, int DV_, bool FP8_>
 struct MfmaCfg {
   static constexpr int DN = DN_, DR = DR_, DV = DV_;
   static constexpr bool FP8 = FP8_;
-  static constexpr int BM = kBlockM_Mfma;  // 128 query rows per item
+  static constexpr int BM = kBlockM_Mfma;  // 256 query rows per item
   static constexpr int BN = kBlockN_Mfma;  // 64 keys per block
-  static constexpr int WAVES = BM / 32;
+  static constexpr int WAVES = BM / 32;    // 8 waves, two per SIMD
   static constexpr int THREADS = WAVES * kWave;
-  static constexpr int EB = FP8 ? 1 : 2;    // bytes per Q/K nope element
-  static constexpr int K_RB = DN * EB;      // bytes per K nope row
-  static constexpr int R_RB = DR * 2;       // bytes per K rope row
-  static constexpr int V_RB = DV * 2;       // bytes per V row
-  // LDS: a K ring and a V ring of two slots each.
+  static constexpr int EB = FP8 ? 1 : 2;   // bytes per Q/K nope element
+  static constexpr int K_RB = DN * EB;     // bytes per K nope row
+  static constexpr int R_RB = DR * 2;      // bytes per K rope row
+  static constexpr int V_RB = DV * 2;      // bytes per V row
+  // LDS: [K0 | K1 | K2 | K3 | V0 | V1 | V2]; block b lives in K slot b % 4
+  // and V slot b % 3.
   //   K slot: K nope rows | K rope rows | k_scale (fp8)      V slot: V rows
-  //   [K0 | K1 | V0 | V1]
+  static constexpr int NKS = 4, NVS = 3;
+  static constexpr int K_RP = K_RB + 16;               // padded K row pitch
+  static constexpr int R_RP = DR > 0 ? R_RB + 16 : 0;  // padded rope row pitch
   static constexpr int K_OFF = 0;                      // inside a K slot
-  static constexpr int R_OFF = BN * K_RB;              // inside a K slot
-  static constexpr int KS_OFF = R_OFF + BN * R_RB;     // inside a K slot
-  static constexpr int KSLOT = KS_OFF + (FP8 ? 256 : 0);  // 64 floats, padded to 256 B
+  static constexpr int R_OFF = BN * K_RP;              // inside a K slot
+  static constexpr int KS_OFF = R_OFF + BN * R_RP;     // inside a K slot
+  static constexpr int KSLOT = (KS_OFF + (FP8 ? 256 : 0) + 255) / 256 * 256;
   static constexpr int VSLOT = BN * V_RB;
-  static constexpr int V_BASE = 2 * KSLOT;
-  static constexpr int LDS = V_BASE + 2 * VSLOT;
-  // two workgroups per CU when the rings fit twice in 160 KiB
-  static constexpr int OCC = 2 * LDS + 64 <= 160 * 1024 ? 2 : 1;
+  static constexpr int V_BASE = NKS * KSLOT;
+  static constexpr int JUNK = V_BASE + NVS * VSLOT;  // 1 KiB sink for padding DMA ops
+  static constexpr int LDS = JUNK + 1024;
+  static constexpr int OCC = 1;              // one workgroup (8 waves) per CU
   static constexpr int O_ROW = DV * 2 + 16;  // epilogue staging row stride
   static constexpr int QK_STEPS = FP8 ? DN / 64 : DN / 16;  // nope MFMA k-steps
   static constexpr int ROPE_STEPS = DR / 16;
-  static constexpr int S_STEPS = QK_STEPS + ROPE_STEPS;   // per 32-key tile
-  static constexpr int NA = 2 * S_STEPS;                  // S products per block
+  static constexpr int S_STEPS = QK_STEPS + ROPE_STEPS;  // S products per sub-tile
   static constexpr int DV_TILES = DV / 32;
-  static constexpr int NB = 4 * DV_TILES;                 // P V products per block
+  static constexpr int NPV = 2 * DV_TILES;  // P V products per sub-tile
+  // 1 KiB DMA instructions per block and region; wave w issues instructions
+  // w, w + WAVES, ... of each region (the fp8 k_scale: wave 0, one dword per
+  // lane).  Every wave issues the same N_OPS instructions per block: the
+  // ones past a region's end, another wave's k_scale and those of a block
+  // that does not exist read nothing (empty buffer range) and land in the
+  // JUNK sink, so one vmcnt(N_OPS) wait fits every wave and every block.
+  static constexpr int K_INST = BN * K_RP / 1024;
+  static constexpr int R_INST = BN * R_RP / 1024;
+  static constexpr int V_INST = BN * V_RB / 1024;
+  static constexpr int K_DMA = (K_INST + WAVES - 1) / WAVES;
+  static constexpr int R_DMA = (R_INST + WAVES - 1) / WAVES;
+  static constexpr int KS_DMA = FP8 ? 1 : 0;
+  static constexpr int V_DMA = V_INST / WAVES;
+  static constexpr int N_OPS = K_DMA + R_DMA + KS_DMA + V_DMA;
 
   static_assert(!FP8 || DR == 0, "fp8 Q/K carry no rope part");
   static_assert(K_RB == 128 || K_RB == 256, "K rows of 128 or 256 bytes");
   static_assert(DR == 0 || R_RB == 128, "rope rows of 128 bytes");
   static_assert(V_RB == 128 || V_RB == 256, "V rows of 128 or 256 bytes");
-  static_assert((BN * K_RB / 1024) % WAVES == 0 && (BN * R_RB / 1024) % WAVES == 0 &&
-                    (BN * V_RB / 1024) % WAVES == 0,
-                "DMA instructions split evenly over the waves");
-  static_assert(KSLOT % 256 == 0 && VSLOT % 256 == 0, "slots keep 256-byte row alignment");
+  static_assert(K_INST * 1024 == BN * K_RP && R_INST * 1024 == BN * R_RP &&
+                    V_INST * 1024 == BN * V_RB,
+                "regions are whole KiB");
+  static_assert(V_DMA * WAVES == V_INST && V_DMA >= 1, "V DMA splits evenly over the waves");
+  static_assert(N_OPS <= 15, "vmcnt immediates");
+  static_assert(V_BASE % 256 == 0 && VSLOT % 256 == 0, "V rows keep 256-byte alignment");
   static_assert(WAVES * 32 * O_ROW <= LDS, "epilogue staging must fit in the rings");
-  static_assert(LDS <= 160 * 1024, "LDS per workgroup");
+  static_assert(LDS + 64 <= 160 * 1024, "LDS per workgroup");
 };
 
-// Chunk swizzles (position of 16-byte chunk c of row r = c ^ swz(r)).
-// K regions are read as A operands: 16 lanes (or 8 on a 32-bank LDS) read
-// the same chunk of 16 (8) consecutive rows in one cycle, which the XOR
-// spreads over distinct banks.
-__device__ __forceinline__ int swz_k256(int r) { return r & 15; }
-__device__ __forceinline__ int swz_k128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-// V rows are read by ds_read_b64_tr_b16: one instruction touches 4 (per 16
-// lanes) or 8 consecutive keys at 2 or 4 chunks each; the XOR keeps both the
-// 16- and the 32-lane groups on distinct banks.
+// XOR swizzle of V rows (position of 16-byte chunk c of key row k =
+// c ^ swz_v(k)).  ds_read_b64_tr_b16 touches 4 (per 16 lanes) or 8
+// consecutive keys at 2 or 4 chunks each; the XOR keeps both the 16- and
+// the 32-lane groups on distinct banks.
 __device__ __forceinline__ int swz_v256(int k) {
   return (4 * (k & 3)) ^ (((k ^ (k >> 1)) & 1) << 1);
 }
 __device__ __forceinline__ int swz_v128(int k) { return 2 * (k & 3); }
-
-template <int RB>
-__device__ __forceinline__ int swz_k(int r) {
-  return RB == 256 ? swz_k256(r) : swz_k128(r);
-}
 template <int RB>
 __device__ __forceinline__ int swz_v(int k) {
   return RB == 256 ? swz_v256(k) : swz_v128(k);
 }
 
-// Keep the compiler from moving anything across this point (the explicit
-// pipeline slots below are laid out in source order).
+// Keep the compiler from moving anything across this point (step
+// boundaries; inside a step the machine scheduler interleaves the
+// independent softmax work with the matrix-core ops).
 #define MHA_SLOT_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 template <int I, int N, class F>
@@ -143,6 +161,13 @@ __device__ __forceinline__ void static_for(F&& f) {
     f(std::integral_constant<int, I>{});
     static_for<I + 1, N>(f);
   }
+}
+
+// s_waitcnt with only the vector-memory counter: vmcnt(N), N < 16.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
 template <class C>
@@ -156,7 +181,7 @@ struct MfmaKernel {
   // else in these kernels keeps a value in m0.)  Issued from inline assembly
   // so that the compiler does not treat it as a pending write to every LDS
   // address (it would otherwise wait for it before each LDS read of the
-  // other slots); completion is awaited explicitly with vmcnt(0) before the
+  // other slots); completion is awaited explicitly with vmcnt before the
   // barrier that publishes the slot.
   static __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t lds_addr,
                                                uint32_t voff) {
@@ -176,6 +201,13 @@ struct MfmaKernel {
         : "s"(lds_addr), "v"(voff), "s"(rsrc)
         : "memory");
   }
+  // Wait for this wave's DMA down to N outstanding instructions, then the
+  // workgroup barrier (no fence: the compiler would add a vmcnt(0) wait).
+  template <int N>
+  static __device__ __forceinline__ void publish() {
+    wait_vm<N>();
+    asm volatile("s_barrier" ::: "memory");
+  }
   // Raw buffer resource (stride 0) over [base, base + bytes) in SGPRs.
   static __device__ __forceinline__ i32x4 rsrc_of(const void* base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -187,91 +219,180 @@ struct MfmaKernel {
     return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
   }
 
-  // This wave's share of the DMA of one row-major region of BN rows of RB
-  // bytes.  Instruction n covers rows RPI*n .. RPI*n+RPI-1; lane i fills
+  // Per-lane source offset of DMA instruction n of a K region of BN rows of
+  // RB bytes stored at pitch RB + 16: lane i fills 16-byte unit 64n + i of
+  // the region, i.e. chunk (64n + i) % (RB/16 + 1) of row (64n + i) /
+  // (RB/16 + 1); the pad unit gets an offset past every buffer (zeros).
+  template <int RB>
+  static __device__ __forceinline__ uint32_t dma_k_lane_off(int n, int lane, int row_stride) {
+    constexpr int UPR = RB / 16 + 1;  // 16-byte units per padded row
+    const int q = 64 * n + lane;
+    const int row = q / UPR, chunk = q % UPR;
+    return chunk == UPR - 1 ? 0x80000000u : (uint32_t)(row * row_stride + chunk * 16);
+  }
+  // Per-lane source offset of DMA instruction n of an unpadded, swizzled V
+  // region: instruction n covers rows RPI*n .. RPI*n+RPI-1; lane i fills
   // position i % CPR of row RPI*n + i / CPR with the chunk that the swizzle
   // puts there.
-  template <int RB, bool VREGION>
-  static __device__ __forceinline__ void dma_region(const char* lds_region, const i32x4& rsrc,
-                                                    int row_stride_bytes, int wave, int lane) {
+  template <int RB>
+  static __device__ __forceinline__ uint32_t dma_v_lane_off(int n, int lane, int row_stride) {
     constexpr int CPR = RB / 16, RPI = 1024 / RB;
-    constexpr int INSTS = C::BN * RB / 1024;
-    constexpr int PER_WAVE = INSTS / C::WAVES;
-    const uint32_t base = lds_addr_of(lds_region);
-#pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int n = wave * PER_WAVE + j;
-      const int row = RPI * n + lane / CPR;
-      const int pos = lane % CPR;
-      const int chunk = pos ^ (VREGION ? swz_v<RB>(row) : swz_k<RB>(row));
-      dma16(rsrc, __builtin_amdgcn_readfirstlane(base + 1024 * n),
-            (uint32_t)(row * row_stride_bytes + chunk * 16));
-    }
+    const int row = RPI * n + lane / CPR;
+    const int chunk = (lane % CPR) ^ swz_v<RB>(row);
+    return (uint32_t)(row * row_stride + chunk * 16);
   }
 
-  struct Rows {
-    size_t row0;    // first [T, Hkv] row of the block
-    uint32_t span;  // [T, Hkv] rows touched by the block's keys
+  // This wave's DMA source offsets (fixed for the kernel: they depend on the
+  // head stride only).
+  struct DmaLanes {
+    uint32_t k[C::K_DMA];
+    uint32_t r[C::R_DMA > 0 ? C::R_DMA : 1];
+    uint32_t v[C::V_DMA];
   };
-  static __device__ __forceinline__ Rows block_rows(const AttnParams& p, int s0, int L, int g,
-                                                   int kbase) {
-    const int rows = min(L - kbase, C::BN);  // >= 1
-    return Rows{(size_t)(s0 + kbase) * p.num_kv_heads + g,
-                (uint32_t)((rows - 1) * p.num_kv_heads + 1)};
-  }
-  // K, K rope and the fp8 k_scale of the block at kbase into a K slot.
-  static __device__ __forceinline__ void load_k(const AttnParams& p, const char* kslot, int wave,
-                                                int lane, int s0, int L, int g, int kbase) {
-    const Rows b = block_rows(p, s0, L, g, kbase);
+  static __device__ __forceinline__ DmaLanes dma_lanes(const AttnParams& p, int wave, int lane) {
+    DmaLanes d;
     const int Hkv = p.num_kv_heads;
-    dma_region<C::K_RB, false>(
-        kslot + C::K_OFF,
-        rsrc_of(static_cast<const char*>(p.k) + b.row0 * C::K_RB, b.span * C::K_RB),
-        Hkv * C::K_RB, wave, lane);
-    if constexpr (C::DR > 0)
-      dma_region<C::R_RB, false>(
-          kslot + C::R_OFF,
-          rsrc_of(static_cast<const char*>(p.k_rope) + b.row0 * C::R_RB, b.span * C::R_RB),
-          Hkv * C::R_RB, wave, lane);
-    if constexpr (C::FP8) {
-      if (wave == 0)
-        dma4(rsrc_of(p.k_scale + b.row0, b.span * 4),
-             __builtin_amdgcn_readfirstlane(lds_addr_of(kslot + C::KS_OFF)),
-             (uint32_t)(lane * Hkv * 4));
+#pragma unroll
+    for (int i = 0; i < C::K_DMA; ++i)
+      d.k[i] = dma_k_lane_off<C::K_RB>(wave + C::WAVES * i, lane, Hkv * C::K_RB);
+    if constexpr (C::R_DMA > 0) {
+#pragma unroll
+      for (int i = 0; i < C::R_DMA; ++i)
+        d.r[i] = dma_k_lane_off<C::R_RB>(wave + C::WAVES * i, lane, Hkv * C::R_RB);
+    }
+#pragma unroll
+    for (int i = 0; i < C::V_DMA; ++i)
+      d.v[i] = dma_v_lane_off<C::V_RB>(wave + C::WAVES * i, lane, Hkv * C::V_RB);
+    return d;
+  }
+
+  // One batch of the DMA pipeline: the K side of block kblk and the V of
+  // block vblk (different blocks), as first [T, Hkv] row and row span
+  // (span 0: the block does not exist) and destination slots.
+  struct BlockDma {
+    uint32_t krow, vrow;  // [T, Hkv] row index (T * Hkv < 2^32: K alone would pass 512 GB)
+    int kspan, vspan;
+    uint32_t kdst, vdst;           // LDS slot addresses
+  };
+  static __device__ __forceinline__ BlockDma block_dma(const AttnParams& p, const char* smem,
+                                                      int s0, int L, int g, int kblk, int vblk,
+                                                      int nblocks) {
+    const int Hkv = p.num_kv_heads;
+    BlockDma b;
+    const bool kon = kblk >= 0 && kblk < nblocks;
+    const bool von = vblk >= 0 && vblk < nblocks;
+    const int kk = kon ? kblk * C::BN : 0, vk = von ? vblk * C::BN : 0;
+    b.krow = (uint32_t)(s0 + kk) * (uint32_t)Hkv + (uint32_t)g;
+    b.vrow = (uint32_t)(s0 + vk) * (uint32_t)Hkv + (uint32_t)g;
+    b.kspan = kon ? (min(L - kk, C::BN) - 1) * Hkv + 1 : 0;
+    b.vspan = von ? (min(L - vk, C::BN) - 1) * Hkv + 1 : 0;
+    b.kdst = lds_addr_of(smem + (kon ? (kblk % C::NKS) * C::KSLOT : C::JUNK));
+    b.vdst = lds_addr_of(smem + (von ? C::V_BASE + (vblk % C::NVS) * C::VSLOT : C::JUNK));
+    return b;
+  }
+  // DMA op OP of this wave (K nope, K rope, fp8 k_scale, V, in that order).
+  // Branch-free: a padding op gets an empty range and the JUNK destination.
+  template <int OP>
+  static __device__ __forceinline__ void dma_op(const AttnParams& p, const char* smem,
+                                                const BlockDma& b, const DmaLanes& d, int wave,
+                                                int lane) {
+    const uint32_t junk = lds_addr_of(smem + C::JUNK);
+    if constexpr (OP < C::K_DMA) {
+      const int n = wave + C::WAVES * OP;
+      const bool real = (C::K_INST % C::WAVES == 0 || n < C::K_INST) && b.kspan > 0;
+      dma16(rsrc_of(static_cast<const char*>(p.k) + (size_t)b.krow * C::K_RB,
+                    real ? (uint32_t)b.kspan * C::K_RB : 0u),
+            __builtin_amdgcn_readfirstlane(real ? b.kdst + C::K_OFF + 1024 * n : junk), d.k[OP]);
+    } else if constexpr (OP < C::K_DMA + C::R_DMA) {
+      constexpr int I = OP - C::K_DMA;
+      const int n = wave + C::WAVES * I;
+      const bool real = (C::R_INST % C::WAVES == 0 || n < C::R_INST) && b.kspan > 0;
+      dma16(rsrc_of(static_cast<const char*>(p.k_rope) + (size_t)b.krow * C::R_RB,
+                    real ? (uint32_t)b.kspan * C::R_RB : 0u),
+            __builtin_amdgcn_readfirstlane(real ? b.kdst + C::R_OFF + 1024 * n : junk), d.r[I]);
+    } else if constexpr (OP < C::K_DMA + C::R_DMA + C::KS_DMA) {
+      const bool real = wave == 0 && b.kspan > 0;
+      dma4(rsrc_of(p.k_scale + b.krow, real ? (uint32_t)b.kspan * 4 : 0u),
+           __builtin_amdgcn_readfirstlane(real ? b.kdst + C::KS_OFF : junk),
+           (uint32_t)(lane * p.num_kv_heads * 4));
+    } else {
+      constexpr int I = OP - C::K_DMA - C::R_DMA - C::KS_DMA;
+      const bool real = b.vspan > 0;
+      dma16(rsrc_of(static_cast<const char*>(p.v) + (size_t)b.vrow * C::V_RB,
+                    real ? (uint32_t)b.vspan * C::V_RB : 0u),
+            __builtin_amdgcn_readfirstlane(real ? b.vdst + 1024 * (wave + C::WAVES * I) : junk),
+            d.v[I]);
     }
   }
-  // V of the block at kbase into a V slot.
-  static __device__ __forceinline__ void load_v(const AttnParams& p, const char* vslot, int wave,
-                                                int lane, int s0, int L, int g, int kbase) {
-    const Rows b = block_rows(p, s0, L, g, kbase);
-    dma_region<C::V_RB, true>(
-        vslot, rsrc_of(static_cast<const char*>(p.v) + b.row0 * C::V_RB, b.span * C::V_RB),
-        p.num_kv_heads * C::V_RB, wave, lane);
+  static __device__ __forceinline__ void dma_all(const AttnParams& p, const char* smem,
+                                                 const BlockDma& b, const DmaLanes& d, int wave,
+                                                 int lane) {
+    static_for<0, C::N_OPS>(
+        [&](auto oc) { dma_op<decltype(oc)::value>(p, smem, b, d, wave, lane); });
+  }
+  // The ops whose place in a step of NS slots is slot SLOT.
+  template <int SLOT, int NS>
+  static __device__ __forceinline__ void dma_at(const AttnParams& p, const char* smem,
+                                                const BlockDma& b, const DmaLanes& d, int wave,
+                                                int lane) {
+    static_for<0, C::N_OPS>([&](auto oc) {
+      constexpr int OP = decltype(oc)::value;
+      if constexpr (OP * NS / C::N_OPS == SLOT) dma_op<OP>(p, smem, b, d, wave, lane);
+    });
   }
 
   // ------------------------------------------------------------ operands
 
-  // A operand of S product a of a block: 32-key tile kt = a % 2 (the two
-  // tiles alternate, so consecutive products are independent), depth step
-  // a / 2 (nope steps first, then rope steps).
-  static __device__ __forceinline__ QFrag s_frag(const char* kslot, int a, int lane32, int hf) {
-    const int kt = a & 1, s = a >> 1;
-    const int r = kt * 32 + lane32;
+  // LDS byte addresses.  Operand addresses are a per-lane part (fixed for
+  // the kernel) plus the slot of the step plus an immediate; the sum of the
+  // first two is made opaque once per step, so that the compiler neither
+  // hoists one address register per immediate out of the loop nor loses the
+  // immediate offsets of the reads.
+  typedef __attribute__((address_space(3))) char lchar;
+  static __device__ __forceinline__ const lchar* lp(uint32_t a) {
+    return reinterpret_cast<const lchar*>(static_cast<uintptr_t>(a));
+  }
+  static __device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+  }
+  struct Lanes {
+    uint32_t k;               // K nope operand: row lane32, this lane half's bytes
+    uint32_t r;               // K rope operand
+    uint32_t v[C::DV_TILES];  // V^T operand of dv tile t (see v_frag)
+  };
+  static __device__ __forceinline__ Lanes lanes_of(int lane) {
+    const int lane32 = lane & 31, hf = lane >> 5;
+    Lanes ln;
+    ln.k = lane32 * C::K_RP + (C::FP8 ? 32 : 16) * hf;
+    ln.r = lane32 * C::R_RP + 16 * hf;
+    const int grp = lane >> 4, s = lane & 15;
+    const int k1 = 4 * (grp >> 1) + (s >> 2);  // key row of the first read (u = 0)
+#pragma unroll
+    for (int t = 0; t < C::DV_TILES; ++t) {
+      const int dv = t * 32 + 16 * (grp & 1) + 4 * (s & 3);  // first of this lane's 4 columns
+      const int c = dv >> 3, sub = (dv & 7) * 2;               // chunk and byte inside it
+      ln.v[t] = k1 * C::V_RB + 16 * (c ^ swz_v<C::V_RB>(k1)) + sub;
+    }
+    return ln;
+  }
+
+  // A operand of S product s of a 32-key sub-tile, from the per-lane K
+  // (nope) and rope addresses of the sub-tile: nope steps first, then rope
+  // steps.  Row pitch is K_RP.
+  static __device__ __forceinline__ QFrag s_frag(uint32_t kt, uint32_t rt, int s) {
     if constexpr (C::FP8) {
-      const char* row = kslot + C::K_OFF + r * C::K_RB;
-      const int sw = swz_k<C::K_RB>(r);
-      const int c0 = 4 * s + 2 * hf;  // 32 bytes = chunks c0, c0 + 1
-      const i32x4 a0 = *reinterpret_cast<const i32x4*>(row + 16 * (c0 ^ sw));
-      const i32x4 a1 = *reinterpret_cast<const i32x4*>(row + 16 * ((c0 + 1) ^ sw));
+      const i32x4 a0 = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
+          lp(kt) + 64 * s);
+      const i32x4 a1 = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
+          lp(kt) + 64 * s + 16);
       return i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
     } else {
-      if (s < C::QK_STEPS) {
-        const char* row = kslot + C::K_OFF + r * C::K_RB;
-        return *reinterpret_cast<const bf16x8*>(row + 16 * ((2 * s + hf) ^ swz_k<C::K_RB>(r)));
-      }
-      const int sr = s - C::QK_STEPS;
-      const char* row = kslot + C::R_OFF + r * C::R_RB;
-      return *reinterpret_cast<const bf16x8*>(row + 16 * ((2 * sr + hf) ^ swz_k<C::R_RB>(r)));
+      if (s < C::QK_STEPS)
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lp(kt) +
+                                                                                  32 * s);
+      return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+          lp(rt) + 32 * (s - C::QK_STEPS));
     }
   }
   static __device__ __forceinline__ f32x16 s_mfma(const QFrag& a, const QFrag& b, f32x16 acc) {
@@ -281,24 +402,20 @@ struct MfmaKernel {
       return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
   }
 
-  // A operand of P V product b of a block: dv tile t = b % DV_TILES, keys
-  // 16u .. 16u+15 with u = b / DV_TILES.  Slot (lane half h, element i)
-  // holds key 16u + 8(i/4) + 4h + i%4 of column 32t + lane % 32, matching the
-  // P^T B-operand slots.  Within each group of 16 lanes, ds_read_b64_tr_b16
+  // A operand of P V product b of a sub-tile, from the per-lane V addresses
+  // of the sub-tile (one per dv tile): dv tile t = b % DV_TILES, keys 16u ..
+  // 16u+15 with u = b / DV_TILES.  Slot (lane half h, element i) holds key
+  // 16u + 8(i/4) + 4h + i%4 of column 32t + lane % 32, matching the P^T
+  // B-operand slots.  Within each group of 16 lanes, ds_read_b64_tr_b16
   // gives lane i, element k, the element i % 4 of the 8 bytes addressed by
   // lane 4k + i/4; so lane s of the group addresses key (base + s/4) at
-  // columns 4(s%4) .. 4(s%4)+3.
-  static __device__ __forceinline__ bf16x8 v_frag(const char* vslot, int b, int lane) {
+  // columns 4(s%4) .. 4(s%4)+3.  The swizzle depends on key % 4 only, so the
+  // keys 16u and 16u + 8 are immediate offsets.
+  static __device__ __forceinline__ bf16x8 v_frag(const uint32_t (&vh)[C::DV_TILES], int b) {
     const int t = b % C::DV_TILES, u = b / C::DV_TILES;
-    const int grp = lane >> 4, s = lane & 15;
-    const int h = grp >> 1;
-    const int dv = t * 32 + 16 * (grp & 1) + 4 * (s & 3);  // first of this lane's 4 columns
-    const int c = dv >> 3, sub = (dv & 7) * 2;               // chunk and byte inside it
-    const int k1 = 16 * u + 4 * h + (s >> 2), k2 = k1 + 8;
-    const char* a1 = vslot + k1 * C::V_RB + 16 * (c ^ swz_v<C::V_RB>(k1)) + sub;
-    const char* a2 = vslot + k2 * C::V_RB + 16 * (c ^ swz_v<C::V_RB>(k2)) + sub;
+    const lchar* a1 = lp(vh[t]) + 16 * u * C::V_RB;
     const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1));
-    const i16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a2));
+    const i16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1 + 8 * C::V_RB));
     const i16x8 r = {r1[0], r1[1], r1[2], r1[3], r2[0], r2[1], r2[2], r2[3]};
     return __builtin_bit_cast(bf16x8, r);
   }
@@ -308,63 +425,44 @@ struct MfmaKernel {
   // Per-wave state of one work item.
   struct State {
     f32x16 o[C::DV_TILES];  // O^T accumulator (lane = query, 16 dv rows per tile)
-    f32x16 st[2];           // S^T of the current block (fp8: k_scale applied)
-    float mx;               // cq * row max of st (valid unless the block is masked)
+    f32x16 st;              // S^T of the current sub-tile (fp8: k_scale applied)
+    float mx;               // cq * row max of st
     float m;                // running max (log2 domain), same in lanes i and i ^ 32
     float l;                // this lane's partial row sum
   };
 
-  static __device__ __forceinline__ void scale_and_max(const char* kslot, int hf, float cq,
-                                                       f32x16 (&st)[2], float& mx) {
-    if constexpr (C::FP8) {
-      const float* ks = reinterpret_cast<const float*>(kslot + C::KS_OFF);
+  // fp8 k_scale and row max of element e of a sub-tile's S (element e of a
+  // lane is key 8(e/4) + 4 hf + e%4 of the sub-tile).
+  static __device__ __forceinline__ void finish_elem(f32x16& s, int e, const float* ks, int hf,
+                                                     float& mx) {
+    if constexpr (C::FP8) s[e] *= ks[8 * (e >> 2) + 4 * hf + (e & 3)];
+    mx = fmaxf(mx, s[e]);
+  }
+
+  // Plain (not pipelined) S of one sub-tile, with the fp8 k_scale, the mask
+  // when asked and the row max: the item's first sub-tile.
+  static __device__ __forceinline__ void s_tile(uint32_t kt, uint32_t rt, const float* ks,
+                                                const QFrag* qf, int hf, float cq, State& w) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+    for (int r = 0; r < 16; ++r) w.st[r] = 0.f;
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 k4 = *reinterpret_cast<const f32x4*>(ks + kt * 32 + 8 * a4 + 4 * hf);
+    for (int s = 0; s < C::S_STEPS; ++s) w.st = s_mfma(s_frag(kt, rt, s), qf[s], w.st);
+    float x = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) st[kt][4 * a4 + r] *= k4[r];
-        }
+    for (int e = 0; e < 16; ++e) finish_elem(w.st, e, ks, hf, x);
+    w.mx = half_max(x) * cq;
+  }
+
+  // Mask of the wave's last sub-tile (first key kb), already in w.st, and its
+  // row max again.
+  static __device__ __forceinline__ void mask_tile(State& w, int kb, int lim, int hf, float cq) {
+    const int rel = (int)opaque((uint32_t)(lim - kb - 4 * hf));  // last visible in-lane key slot
+    float x = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if (8 * (e >> 2) + (e & 3) > rel) w.st[e] = -INFINITY;
+      x = fmaxf(x, w.st[e]);
     }
-    float x = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x = fmaxf(x, st[kt][r]);
-    mx = half_max(x) * cq;
-  }
-
-  // Plain (not pipelined) S of one block from a K slot, with the fp8
-  // k_scale and the row max: used for block 0.
-  static __device__ __forceinline__ void s_block(const char* kslot, const QFrag* qf, int lane32,
-                                                 int hf, float cq, State& w) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) w.st[kt][r] = 0.f;
-#pragma unroll
-    for (int a = 0; a < C::NA; ++a)
-      w.st[a & 1] = s_mfma(s_frag(kslot, a, lane32, hf), qf[a >> 1], w.st[a & 1]);
-    scale_and_max(kslot, hf, cq, w.st, w.mx);
-  }
-
-  // Mask of a block that crosses the causal diagonal or the sequence end
-  // (hidden keys -> -inf) and its row max.
-  static __device__ __forceinline__ void mask_block(State& w, int kbase, int lim, int hf,
-                                                    float cq) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kbase + kt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (key > lim) w.st[kt][r] = -INFINITY;
-      }
-    float x = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x = fmaxf(x, w.st[kt][r]);
     w.mx = half_max(x) * cq;
   }
 
@@ -383,84 +481,90 @@ struct MfmaKernel {
     return w.m == -INFINITY ? 0.f : w.m;
   }
 
-  // Exponentials of elements [LO, HI) of the 32 S values of a lane (element
-  // e is st[e / 16][e % 16]), with each finished pair packed to bf16.
+  // Exponentials of elements [LO, HI) of the sub-tile's 16 S values of a
+  // lane, with each finished pair packed to bf16.
   template <int LO, int HI>
-  static __device__ __forceinline__ void exp_chunk(f32x16 (&st)[2], float cq, float m_use,
-                                                   uint32_t (&pw)[16], float (&ls)[2]) {
+  static __device__ __forceinline__ void exp_chunk(f32x16& st, float cq, float m_use,
+                                                   uint32_t (&pw)[8], float (&ls)[2]) {
 #pragma unroll
     for (int e = LO; e < HI; ++e) {
-      st[e >> 4][e & 15] = fast_exp2(fmaf(st[e >> 4][e & 15], cq, -m_use));
-      ls[e & 1] += st[e >> 4][e & 15];
-      if (e & 1) pw[e >> 1] = pack_bf16x2(st[(e - 1) >> 4][(e - 1) & 15], st[e >> 4][e & 15]);
+      st[e] = fast_exp2(fmaf(st[e], cq, -m_use));
+      ls[e & 1] += st[e];
+      if (e & 1) pw[e >> 1] = pack_bf16x2(st[e - 1], st[e]);
     }
   }
 
-  // One pipelined block.  NEXT: compute S of the following block (K slot
-  // kn) alongside.  On entry w.st holds this block's S (scaled, masked) and
-  // w.mx its row max; on exit they hold the next block's.
-  template <bool NEXT>
-  static __device__ __forceinline__ void block(State& w, const char* kn, const char* vslot,
-                                               const QFrag* qf, int lane, int lane32, int hf,
-                                               float cq) {
+  // Where the operands of one step live: K (and rope, k_scale) rows of the
+  // next sub-tile, V rows of this one.
+  struct StepSrc {
+    uint32_t kn, rn;           // next sub-tile's K nope / rope operand addresses (per lane)
+    const float* ks;           // next sub-tile's k_scale (fp8)
+    uint32_t vh[C::DV_TILES];  // this sub-tile's V operand addresses (per lane)
+  };
+
+  // One pipelined sub-tile step.  NEXT: compute S of the following sub-tile
+  // alongside (k_scale and row max included, no mask).  DMA: issue the
+  // block's DMA ops in this step's slots.  On entry w.st holds this
+  // sub-tile's S (scaled, masked) and w.mx its row max; on exit they hold
+  // the next sub-tile's.
+  template <bool NEXT, bool DMA>
+  static __device__ __forceinline__ void step(State& w, const StepSrc& src, const QFrag* qf,
+                                              int lane, int lane32, int hf, float cq,
+                                              const AttnParams& p, const char* smem,
+                                              const BlockDma& bd, const DmaLanes& dl, int wave) {
+    constexpr int NS = (NEXT ? C::S_STEPS : 0) + C::NPV;  // matrix-core slots
     const float m_use = correct(w);
-    uint32_t pw[16];  // P as packed bf16 pairs: pw[4u + i] = dword i of B operand u
+    uint32_t pw[8];  // P as packed bf16 pairs: pw[4u + i] = dword i of B operand u
     float ls[2] = {0.f, 0.f};
-    f32x16 sn[2];
+    f32x16 sn;
     MHA_SLOT_FENCE();
 
-    // ---- phase A: S products of the next block + exponentials of this one
+    // ---- phase A: S products of the next sub-tile + exponentials of this one
     if constexpr (NEXT) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sn[kt][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sn[r] = 0.f;
       QFrag kf[3];
-      kf[0] = s_frag(kn, 0, lane32, hf);
-      kf[1] = s_frag(kn, 1, lane32, hf);
-      static_for<0, C::NA>([&](auto ac) {
+      kf[0] = s_frag(src.kn, src.rn, 0);
+      if constexpr (C::S_STEPS > 1) kf[1] = s_frag(src.kn, src.rn, 1);
+      static_for<0, C::S_STEPS>([&](auto ac) {
         constexpr int a = decltype(ac)::value;
-        if constexpr (a + 2 < C::NA) kf[(a + 2) % 3] = s_frag(kn, a + 2, lane32, hf);
-        sn[a & 1] = s_mfma(kf[a % 3], qf[a >> 1], sn[a & 1]);
-        exp_chunk<a * 32 / C::NA, (a + 1) * 32 / C::NA>(w.st, cq, m_use, pw, ls);
-        MHA_SLOT_FENCE();
+        constexpr int E0 = a * 16 / C::S_STEPS, E1 = (a + 1) * 16 / C::S_STEPS;
+        if constexpr (a + 2 < C::S_STEPS)
+          kf[(a + 2) % 3] = s_frag(src.kn, src.rn, a + 2);
+        sn = s_mfma(kf[a % 3], qf[a], sn);
+        exp_chunk<E0, E1>(w.st, cq, m_use, pw, ls);
+        if constexpr (DMA) dma_at<a, NS>(p, smem, bd, dl, wave, lane);
       });
     } else {
-      exp_chunk<0, 32>(w.st, cq, m_use, pw, ls);
+      exp_chunk<0, 16>(w.st, cq, m_use, pw, ls);
     }
 
-    // ---- phase B: P V products (+ next block's scale and max)
-    bf16x8 pb[4];
+    // ---- phase B: P V products (+ next sub-tile's scale, mask and max)
+    bf16x8 pb[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 2; ++u)
       pb[u] = __builtin_bit_cast(
           bf16x8, i32x4{(int)pw[4 * u], (int)pw[4 * u + 1], (int)pw[4 * u + 2], (int)pw[4 * u + 3]});
     float mxp = -INFINITY;
-    const float* ks = reinterpret_cast<const float*>(kn + C::KS_OFF);
     bf16x8 vf[3];
-    vf[0] = v_frag(vslot, 0, lane);
-    vf[1] = v_frag(vslot, 1, lane);
-    static_for<0, C::NB>([&](auto bc) {
+    vf[0] = v_frag(src.vh, 0);
+    vf[1] = v_frag(src.vh, 1);
+    static_for<0, C::NPV>([&](auto bc) {
       constexpr int b = decltype(bc)::value;
-      if constexpr (b + 2 < C::NB) vf[(b + 2) % 3] = v_frag(vslot, b + 2, lane);
+      if constexpr (b + 2 < C::NPV) vf[(b + 2) % 3] = v_frag(src.vh, b + 2);
       w.o[b % C::DV_TILES] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           vf[b % 3], pb[b / C::DV_TILES], w.o[b % C::DV_TILES], 0, 0, 0);
-      // next block's k_scale and row max over the second half of the slots
-      if constexpr (NEXT && 2 * b >= C::NB) {
-        constexpr int H = C::NB / 2, q = b - C::NB / 2;
+      if constexpr (NEXT) {
 #pragma unroll
-        for (int e = q * 32 / H; e < (q + 1) * 32 / H; ++e) {
-          if constexpr (C::FP8)
-            sn[e >> 4][e & 15] *= ks[(e >> 4) * 32 + 8 * ((e & 15) >> 2) + 4 * hf + (e & 3)];
-          mxp = fmaxf(mxp, sn[e >> 4][e & 15]);
-        }
+        for (int e = b * 16 / C::NPV; e < (b + 1) * 16 / C::NPV; ++e)
+          finish_elem(sn, e, src.ks, hf, mxp);
       }
-      MHA_SLOT_FENCE();
+      if constexpr (DMA) dma_at<(NEXT ? C::S_STEPS : 0) + b, NS>(p, smem, bd, dl, wave, lane);
     });
+    MHA_SLOT_FENCE();
     w.l += ls[0] + ls[1];
     if constexpr (NEXT) {
-      w.st[0] = sn[0];
-      w.st[1] = sn[1];
+      w.st = sn;
       w.mx = half_max(mxp) * cq;
     }
   }
@@ -478,6 +582,9 @@ struct MfmaKernel {
     const char* __restrict__ qp = static_cast<const char*>(p.q);
     const char* __restrict__ qrp = static_cast<const char*>(p.q_rope);
     char* __restrict__ op = static_cast<char*>(p.o);
+    const DmaLanes dl = dma_lanes(p, wave, lane);
+    const Lanes ln = lanes_of(lane);
+    const uint32_t sbase = lds_addr_of(smem);
 
     // wave 0 runs the work-item source; the next item's table entry is read
     // while the current item's first blocks load and published at the first
@@ -509,14 +616,13 @@ struct MfmaKernel {
 
       const int n_kv = p.causal ? min(L, q0 + C::BM) : L;
       const int nblocks = (n_kv + C::BN - 1) / C::BN;
-      // blocks this wave computes (causal: keys up to wq0 + 31 only), and the
-      // leading ones among them that need no mask
-      const int wave_nblocks = p.causal ? min(nblocks, ((wq0 + 31) >> 6) + 1) : nblocks;
-      const int n_full = (p.causal ? min(L, wq0 + 1) : L) / C::BN;
+      // 32-key sub-tiles this wave computes (causal: keys up to wq0 + 31
+      // only; none when all its rows are past the end); only the last can
+      // need the mask
+      const int n_sub = wq0 >= L ? 0
+                        : p.causal ? min((L + 31) >> 5, (wq0 >> 5) + 1)
+                                   : (L + 31) >> 5;
       const int lim = p.causal ? min(L - 1, qi) : L - 1;  // last key visible to this lane
-
-      load_k(p, smem, wave, lane, s0, L, g, 0);
-      load_v(p, smem + C::V_BASE, wave, lane, s0, L, g, 0);
 
       // Q fragments (B operand): lane -> query qi, 8 (bf16) or 32 (fp8)
       // consecutive depth elements per step and lane half; rope steps follow
@@ -559,68 +665,72 @@ struct MfmaKernel {
       w.m = -INFINITY;
       w.l = 0.f;
 
-      // prologue: block 0's K and V (and the next item's entry) land; S_0;
-      // K_1 lands
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
+      // Prologue: batch t of the pipeline is {K_{t+3}, V_{t+2}}; block j
+      // issues batch j.  Batches -3 and -2 ({K_0} and {K_1, V_0}) are waited
+      // for here together with the Q loads (the compiler's own wait for
+      // those could not tell the DMA apart anyway); batch -1 ({K_2, V_1})
+      // goes out after the first S.
+      dma_all(p, smem, block_dma(p, smem, s0, L, g, 0, -1, nblocks), dl, wave, lane);
+      dma_all(p, smem, block_dma(p, smem, s0, L, g, 1, 0, nblocks), dl, wave, lane);
+      wait_vm<0>();
       if (tid == 0) s_item[(it + 1) & 1] = nxt;
       __syncthreads();
-      s_block(smem, qf, lane32, hf, cq, w);
-      if (nblocks > 1) load_k(p, smem + C::KSLOT, wave, lane, s0, L, g, C::BN);
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
+      if (n_sub > 0) {
+        s_tile(opaque(sbase + C::K_OFF + ln.k), opaque(sbase + C::R_OFF + ln.r),
+               reinterpret_cast<const float*>(smem + C::KS_OFF), qf, hf, cq, w);
+        if (n_sub == 1) mask_tile(w, 0, lim, hf, cq);
+      }
+      dma_all(p, smem, block_dma(p, smem, s0, L, g, 2, 1, nblocks), dl, wave, lane);
 
-      // Block j: K_{j+2} -> K slot j%2 and V_{j+1} -> V slot (j+1)%2 go out
-      // first (both slots were last read in block j-1); the block then reads
-      // K slot (j+1)%2 and V slot j%2; every wave ends it at one barrier.
-      // The slot parity is a template argument (blocks are taken in pairs),
-      // so every LDS operand address is a per-lane offset plus a constant.
-      auto issue = [&](auto par, int j) {
-        constexpr int P = decltype(par)::value;
-        if (j + 2 < nblocks) load_k(p, smem + P * C::KSLOT, wave, lane, s0, L, g, (j + 2) * C::BN);
-        if (j + 1 < nblocks)
-          load_v(p, smem + C::V_BASE + (1 - P) * C::VSLOT, wave, lane, s0, L, g, (j + 1) * C::BN);
+      // Block j: sub-steps 2j (S of keys 32..63 of block j, P V of keys
+      // 0..31) and 2j+1 (S of keys 0..31 of block j+1, P V of keys 32..63);
+      // K_{j+3} and V_{j+2} are requested; at the end K_{j+2} and V_{j+1}
+      // (requested in block j-1) must have landed, then one barrier.
+      auto src_of = [&](int i) {
+        // operands of sub-step i: next sub-tile i+1's K, this sub-tile's V
+        const int jn = (i + 1) >> 1, hn = (i + 1) & 1;
+        const uint32_t ks = sbase + (jn % C::NKS) * C::KSLOT;
+        const uint32_t vs =
+            sbase + C::V_BASE + ((i >> 1) % C::NVS) * C::VSLOT + (i & 1) * 32 * C::V_RB;
+        StepSrc s;
+        s.kn = opaque(ks + C::K_OFF + hn * 32 * C::K_RP + ln.k);
+        s.rn = C::DR > 0 ? opaque(ks + C::R_OFF + hn * 32 * C::R_RP + ln.r) : 0u;
+        s.ks = reinterpret_cast<const float*>(smem + (jn % C::NKS) * C::KSLOT + C::KS_OFF) + 32 * hn;
+#pragma unroll
+        for (int t = 0; t < C::DV_TILES; ++t) s.vh[t] = opaque(vs + ln.v[t]);
+        return s;
       };
-      auto finish = [&]() {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMA landed
-        __syncthreads();
+      // end of block j: batch j may stay in flight, batch j-1 must be in
+      auto finish = [&]() { publish<C::N_OPS>(); };
+      auto blk = [&](int j) { return block_dma(p, smem, s0, L, g, j + 3, j + 2, nblocks); };
+      using Y = std::true_type;
+      using N = std::false_type;
+      auto run_step = [&](auto next, auto dma, int i, const BlockDma& bd) {
+        step<decltype(next)::value, decltype(dma)::value>(w, src_of(i), qf, lane, lane32, hf, cq,
+                                                          p, smem, bd, dl, wave);
+        // the sub-tile just computed is the wave's last: mask it
+        if (i + 1 == n_sub - 1) mask_tile(w, 32 * (i + 1), lim, hf, cq);
       };
-      auto step = [&](auto next, auto par, int j) {
-        constexpr bool NEXT = decltype(next)::value;
-        constexpr int P = decltype(par)::value;
-        issue(par, j);
-        if (j >= n_full) mask_block(w, j * C::BN, lim, hf, cq);
-        block<NEXT>(w, smem + (1 - P) * C::KSLOT, smem + C::V_BASE + P * C::VSLOT, qf, lane,
-                    lane32, hf, cq);
-        finish();
-      };
-      using Even = std::integral_constant<int, 0>;
-      using Odd = std::integral_constant<int, 1>;
-      using Yes = std::true_type;
-      using No = std::false_type;
-      int j = 0;
-      for (; j + 2 < wave_nblocks; j += 2) {
-        step(Yes{}, Even{}, j);
-        step(Yes{}, Odd{}, j + 1);
-      }
-      if (j + 1 < wave_nblocks) {
-        step(Yes{}, Even{}, j);
-        ++j;
-      }
-      // this wave's last block: no next S
-      if (j & 1)
-        step(No{}, Odd{}, j);
-      else
-        step(No{}, Even{}, j);
-      ++j;
-      // causal: blocks past this wave's last visible key -- keep the
-      // workgroup's DMA / barrier rhythm only
-      for (; j < nblocks; ++j) {
-        if (j & 1)
-          issue(Odd{}, j);
-        else
-          issue(Even{}, j);
+      // A wave's last sub-tile also computes the S of a sub-tile that does
+      // not exist (from whatever its K slot holds); that S is never used,
+      // which costs one sub-tile of S products per wave and item but keeps
+      // a single step body per position in the block.
+      for (int j = 0; j < nblocks; ++j) {
+        const BlockDma bd = blk(j);
+        const int i0 = 2 * j;
+        if (i0 < n_sub) {
+          run_step(Y{}, Y{}, i0, bd);
+          if (i0 + 1 < n_sub) run_step(Y{}, N{}, i0 + 1, bd);
+        } else {
+          // past this wave's last visible key: keep the workgroup's DMA and
+          // barrier rhythm only
+          dma_all(p, smem, bd, dl, wave, lane);
+        }
         finish();
       }
+      // the last batches requested nothing; drain before the rings are
+      // reused for the output staging
+      wait_vm<0>();
 
       // ---- epilogue
       const float lt = half_sum(w.l);

@@ -10,7 +10,7 @@
 namespace mha {
 
 // Query-tile heights of the two kernel families (rows of Q per work item).
-constexpr int kBlockM_Mfma = 128;
+constexpr int kBlockM_Mfma = 256;
 constexpr int kBlockN_Mfma = 64;
 constexpr int kBlockM_F32 = 64;
 constexpr int kBlockN_F32 = 32;

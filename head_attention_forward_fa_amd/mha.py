@@ -129,7 +129,7 @@ def mha_fwd_kernel_info(dtype_code: int, head_dim_nope: int, head_dim_rope: int,
 
 
 def mha_sched_visit(cu_seqlens: torch.Tensor, max_seqlen: int, num_heads: int,
-                    num_kv_heads: int, causal: bool, block_m: int = 128,
+                    num_kv_heads: int, causal: bool, block_m: int = 256,
                     grid: int = 0) -> torch.Tensor:
     """Runs the scheduler alone; returns visit counts [Hq, B, tiles] (int32)."""
     B = cu_seqlens.numel() - 1

@@ -76,7 +76,7 @@ typedef enum {
  *   batch       number of sequences, >= 1
  *   max_seqlen  >= every sequence length; sizes the work table (num_heads *
  *               batch * ceil(max_seqlen / block_m) entries, block_m = 64
- *               for float32 and 128 for bf16 / fp8).  0 means every
+ *               for float32 and 256 for bf16 / fp8).  0 means every
  *               sequence is empty: the scalar arguments are still checked,
  *               but nothing is read, written or launched and the tensor
  *               pointers may be NULL.  When the lengths
@@ -152,7 +152,7 @@ int mha_fwd_kernel_info(int32_t dtype, int32_t head_dim_nope, int32_t head_dim_r
  * visits[h * (batch * tiles) + b * tiles + qtile], tiles =
  * ceil(max_seqlen / block_m).  visits is a caller-owned device int32 array of
  * num_heads * batch * tiles entries, zeroed by the caller.  block_m is 64 or
- * 128 (the float32 and MFMA kernels' query tiles).  Every existing item must
+ * 256 (the float32 and MFMA kernels' query tiles).  Every existing item must
  * end with exactly one visit.
  */
 int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,

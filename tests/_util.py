@@ -103,7 +103,8 @@ def sample_tokens(inp: Inputs, n_random: int = 24, seed: int = 1):
         s0, s1 = int(cu[b]), int(cu[b + 1])
         if s1 == s0:
             continue
-        for i in (0, 1, 63, 64, 127, 128, 129, s1 - s0 - 2, s1 - s0 - 1):
+        for i in (0, 1, 31, 32, 63, 64, 127, 128, 255, 256, 257, 4095, 4096,
+                  s1 - s0 - 2, s1 - s0 - 1):
             if 0 <= i < s1 - s0:
                 toks.add(s0 + i)
     if inp.total_tokens:

@@ -97,10 +97,12 @@ def test_supported_set():
 
 def test_sched_visit_validation():
     lib = nat.load()
-    assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 32, 0, FAKE, None) == nat.MHA_ERR_INVALID_ARG
-    assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 128, 0, None, None) == nat.MHA_ERR_INVALID_ARG
-    assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 128, -1, FAKE, None) == nat.MHA_ERR_INVALID_ARG
-    assert lib.mha_sched_visit(FAKE, 1, 0, 4, 2, 1, 128, 0, FAKE, None) == nat.MHA_OK
+    for bad_block_m in (32, 128):
+        assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, bad_block_m, 0, FAKE,
+                                   None) == nat.MHA_ERR_INVALID_ARG
+    assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 256, 0, None, None) == nat.MHA_ERR_INVALID_ARG
+    assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 256, -1, FAKE, None) == nat.MHA_ERR_INVALID_ARG
+    assert lib.mha_sched_visit(FAKE, 1, 0, 4, 2, 1, 256, 0, FAKE, None) == nat.MHA_OK
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -1,7 +1,7 @@
 """HIP path vs the float64 oracle, element by element, through the C ABI.
 
-Small cases (seconds for the oracle) span several 128-row query tiles and
-64-key blocks with ragged tails, GQA, empty sequences, the nope/rope split and
+Small cases (seconds for the oracle) span several 256-row query tiles and
+64-key blocks (enough of them to wrap the kernel's 4-slot K and 3-slot V rings) with ragged tails, GQA, empty sequences, the nope/rope split and
 fp8; the five named workloads run at full size with the oracle evaluated on
 sampled rows (first, last, tile-boundary and random tokens, every head).
 Tolerances (max-abs): O 1e-4 fp32, 2e-2 bf16, 6e-2 fp8; LSE 1e-3.
@@ -25,11 +25,15 @@ SMALL = [
     ("bf16", [1, 129, 0, 517, 64], 8, 2, 128, 0, 128, False),
     ("bf16", [200, 77], 4, 1, 64, 0, 64, True),
     ("bf16", [200, 77], 4, 1, 64, 0, 64, False),
+    ("bf16", [1100], 2, 2, 128, 0, 128, True),
+    ("bf16", [1100, 31], 2, 1, 128, 0, 128, False),
     ("bf16", [333], 4, 4, 128, 64, 128, True),
+    ("bf16", [650], 2, 2, 128, 64, 128, False),
     ("bf16", [190, 5], 4, 2, 128, 64, 128, False),
     ("fp8", [300, 50], 4, 4, 128, 0, 128, True),
     ("fp8", [300, 50], 4, 4, 128, 0, 128, False),
     ("fp8", [257], 8, 2, 128, 0, 128, True),
+    ("fp8", [900], 2, 2, 128, 0, 128, True),
     ("f32", [100, 3], 2, 2, 128, 0, 128, True),
     ("f32", [70], 2, 1, 128, 64, 128, True),
     ("f32", [130, 1], 2, 2, 64, 0, 64, True),
@@ -114,7 +118,7 @@ def test_all_sequences_empty_and_zero_max_seqlen():
 
 def test_overflowing_lengths_are_refused_without_writes():
     # max_seqlen 128 sizes the table for one tile per (sequence, head); a
-    # 300-token sequence needs three, so the device refuses and writes nothing
+    # 300-token sequence needs two, so the device refuses and writes nothing
     from head_attention_forward_fa_amd import mha_fwd
     inp = mi.make_inputs(dtype="bf16", seqlens=[300], num_heads=2, num_kv_heads=2,
                          head_dim_nope=128, v_dim=128, causal=True, seed=5)
@@ -127,7 +131,7 @@ def test_overflowing_lengths_are_refused_without_writes():
     assert bool((out == 7.0).all()) and bool((lse == 7.0).all())
 
 
-@pytest.mark.parametrize("block_m", [64, 128])
+@pytest.mark.parametrize("block_m", [64, 256])
 @pytest.mark.parametrize("grid", [0, 1, 7, 1000])
 def test_scheduler_visits_every_item_once(block_m, grid):
     from head_attention_forward_fa_amd import mha_sched_visit
@@ -156,10 +160,10 @@ def test_scheduler_many_groups_index_mode():
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     hq, hkv = 8, 4
     mx = int(lens.max())
-    visits = mha_sched_visit(torch.from_numpy(cu).cuda(), mx, hq, hkv, False, 128, 0)
+    visits = mha_sched_visit(torch.from_numpy(cu).cuda(), mx, hq, hkv, False, 256, 0)
     torch.cuda.synchronize()
-    tiles = (mx + 127) // 128
+    tiles = (mx + 255) // 256
     want = np.zeros((hq, len(lens), tiles), dtype=np.int32)
     for b, L in enumerate(lens):
-        want[:, b, : (L + 127) // 128] = 1
+        want[:, b, : (L + 255) // 256] = 1
     assert np.array_equal(visits.cpu().numpy(), want)
