@@ -87,10 +87,10 @@ struct MfmaCfg {
   static constexpr int K_RB = DN * EB;     // bytes per K nope row
   static constexpr int R_RB = DR * 2;      // bytes per K rope row
   static constexpr int V_RB = DV * 2;      // bytes per V row
-  // LDS: [K0 | K1 | K2 | K3 | V0 | V1 | V2]; block b lives in K slot b % 4
-  // and V slot b % 3.
+  // LDS: [K slots | V slots | sink]; block b lives in K slot b % NKS and V
+  // slot b % NVS.
   //   K slot: K nope rows | K rope rows | k_scale (fp8)      V slot: V rows
-  static constexpr int NKS = 4, NVS = 3;
+  static constexpr int NVS = 4;
   static constexpr int K_RP = K_RB + 16;               // padded K row pitch
   static constexpr int R_RP = DR > 0 ? R_RB + 16 : 0;  // padded rope row pitch
   static constexpr int K_OFF = 0;                      // inside a K slot
@@ -98,6 +98,9 @@ struct MfmaCfg {
   static constexpr int KS_OFF = R_OFF + BN * R_RP;     // inside a K slot
   static constexpr int KSLOT = (KS_OFF + (FP8 ? 256 : 0) + 255) / 256 * 256;
   static constexpr int VSLOT = BN * V_RB;
+  // 4 K slots when they fit next to the V ring, else 3 (the rope layout)
+  static constexpr int NKS = 4 * KSLOT + NVS * BN * V_RB + 1024 + 64 <= 160 * 1024 ? 4 : 3;
+  static constexpr int KLEAD = NKS - 1;  // blocks between a K block's request and its use
   static constexpr int V_BASE = NKS * KSLOT;
   static constexpr int JUNK = V_BASE + NVS * VSLOT;  // 1 KiB sink for padding DMA ops
   static constexpr int LDS = JUNK + 1024;
@@ -425,51 +428,53 @@ struct MfmaKernel {
   // Per-wave state of one work item.
   struct State {
     f32x16 o[C::DV_TILES];  // O^T accumulator (lane = query, 16 dv rows per tile)
-    f32x16 st;              // S^T of the current sub-tile (fp8: k_scale applied)
-    float mx;               // cq * row max of st
+    f32x16 st;              // S^T of the sub-tile awaiting its softmax half-step
+    uint32_t pw[8];         // P of the sub-tile awaiting its product half-step,
+                            // packed bf16 pairs: pw[4u + i] = dword i of B operand u
     float m;                // running max (log2 domain), same in lanes i and i ^ 32
     float l;                // this lane's partial row sum
   };
 
-  // fp8 k_scale and row max of element e of a sub-tile's S (element e of a
-  // lane is key 8(e/4) + 4 hf + e%4 of the sub-tile).
-  static __device__ __forceinline__ void finish_elem(f32x16& s, int e, const float* ks, int hf,
-                                                     float& mx) {
-    if constexpr (C::FP8) s[e] *= ks[8 * (e >> 2) + 4 * hf + (e & 3)];
-    mx = fmaxf(mx, s[e]);
-  }
-
-  // Plain (not pipelined) S of one sub-tile, with the fp8 k_scale, the mask
-  // when asked and the row max: the item's first sub-tile.
-  static __device__ __forceinline__ void s_tile(uint32_t kt, uint32_t rt, const float* ks,
-                                                const QFrag* qf, int hf, float cq, State& w) {
+  // Plain S of one sub-tile (the item's first).
+  static __device__ __forceinline__ void s_tile(uint32_t kt, uint32_t rt, const QFrag* qf,
+                                                State& w) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) w.st[r] = 0.f;
 #pragma unroll
     for (int s = 0; s < C::S_STEPS; ++s) w.st = s_mfma(s_frag(kt, rt, s), qf[s], w.st);
-    float x = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) finish_elem(w.st, e, ks, hf, x);
-    w.mx = half_max(x) * cq;
   }
 
-  // Mask of the wave's last sub-tile (first key kb), already in w.st, and its
-  // row max again.
-  static __device__ __forceinline__ void mask_tile(State& w, int kb, int lim, int hf, float cq) {
-    const int rel = (int)opaque((uint32_t)(lim - kb - 4 * hf));  // last visible in-lane key slot
+  // Softmax half-step of a sub-tile whose S is in w.st: fp8 k_scale, the mask
+  // when it is the wave's last sub-tile (keys past `rel` in lane-relative
+  // numbering hidden), row max, lazy correction of O and l, exponentials,
+  // row sums and the bf16 packing of P into w.pw.  Element e of a lane is key
+  // 8(e/4) + 4 hf + e%4 of the sub-tile.
+  template <int OP0, int OP1>
+  static __device__ __forceinline__ void xphase(State& w, const float* ks, int hf, float cq,
+                                                bool mask, int rel, const AttnParams& p,
+                                                const char* smem, const BlockDma& bd,
+                                                const DmaLanes& dl, int wave, int lane) {
+    MHA_SLOT_FENCE();
+    // this half-step's share of the block's DMA ops
+    static_for<OP0, OP1>([&](auto oc) { dma_op<decltype(oc)::value>(p, smem, bd, dl, wave, lane); });
     float x = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      if (8 * (e >> 2) + (e & 3) > rel) w.st[e] = -INFINITY;
+      if constexpr (C::FP8) w.st[e] *= ks[8 * (e >> 2) + 4 * hf + (e & 3)];
       x = fmaxf(x, w.st[e]);
     }
-    w.mx = half_max(x) * cq;
-  }
-
-  // Lazy correction of the running statistics; returns the exponent offset.
-  static __device__ __forceinline__ float correct(State& w) {
-    if (wave_any(w.mx > w.m + 8.0f)) {
-      const float m_new = fmaxf(w.m, w.mx);
+    if (mask) {
+      x = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (8 * (e >> 2) + (e & 3) > rel) w.st[e] = -INFINITY;
+        x = fmaxf(x, w.st[e]);
+      }
+    }
+    const float mx = half_max(x) * cq;
+    // lazy correction: only when some row's max grew by more than 8
+    if (wave_any(mx > w.m + 8.0f)) {
+      const float m_new = fmaxf(w.m, mx);
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(w.m - m_new);
       w.l *= alpha;
 #pragma unroll
@@ -478,95 +483,62 @@ struct MfmaKernel {
         for (int r = 0; r < 16; ++r) w.o[t][r] *= alpha;
       w.m = m_new;
     }
-    return w.m == -INFINITY ? 0.f : w.m;
-  }
-
-  // Exponentials of elements [LO, HI) of the sub-tile's 16 S values of a
-  // lane, with each finished pair packed to bf16.
-  template <int LO, int HI>
-  static __device__ __forceinline__ void exp_chunk(f32x16& st, float cq, float m_use,
-                                                   uint32_t (&pw)[8], float (&ls)[2]) {
-#pragma unroll
-    for (int e = LO; e < HI; ++e) {
-      st[e] = fast_exp2(fmaf(st[e], cq, -m_use));
-      ls[e & 1] += st[e];
-      if (e & 1) pw[e >> 1] = pack_bf16x2(st[e - 1], st[e]);
-    }
-  }
-
-  // Where the operands of one step live: K (and rope, k_scale) rows of the
-  // next sub-tile, V rows of this one.
-  struct StepSrc {
-    uint32_t kn, rn;           // next sub-tile's K nope / rope operand addresses (per lane)
-    const float* ks;           // next sub-tile's k_scale (fp8)
-    uint32_t vh[C::DV_TILES];  // this sub-tile's V operand addresses (per lane)
-  };
-
-  // One pipelined sub-tile step.  NEXT: compute S of the following sub-tile
-  // alongside (k_scale and row max included, no mask).  DMA: issue the
-  // block's DMA ops in this step's slots.  On entry w.st holds this
-  // sub-tile's S (scaled, masked) and w.mx its row max; on exit they hold
-  // the next sub-tile's.
-  template <bool NEXT, bool DMA>
-  static __device__ __forceinline__ void step(State& w, const StepSrc& src, const QFrag* qf,
-                                              int lane, int lane32, int hf, float cq,
-                                              const AttnParams& p, const char* smem,
-                                              const BlockDma& bd, const DmaLanes& dl, int wave) {
-    constexpr int NS = (NEXT ? C::S_STEPS : 0) + C::NPV;  // matrix-core slots
-    const float m_use = correct(w);
-    uint32_t pw[8];  // P as packed bf16 pairs: pw[4u + i] = dword i of B operand u
+    const float m_use = w.m == -INFINITY ? 0.f : w.m;
     float ls[2] = {0.f, 0.f};
-    f32x16 sn;
-    MHA_SLOT_FENCE();
-
-    // ---- phase A: S products of the next sub-tile + exponentials of this one
-    if constexpr (NEXT) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sn[r] = 0.f;
-      QFrag kf[3];
-      kf[0] = s_frag(src.kn, src.rn, 0);
-      if constexpr (C::S_STEPS > 1) kf[1] = s_frag(src.kn, src.rn, 1);
-      static_for<0, C::S_STEPS>([&](auto ac) {
-        constexpr int a = decltype(ac)::value;
-        constexpr int E0 = a * 16 / C::S_STEPS, E1 = (a + 1) * 16 / C::S_STEPS;
-        if constexpr (a + 2 < C::S_STEPS)
-          kf[(a + 2) % 3] = s_frag(src.kn, src.rn, a + 2);
-        sn = s_mfma(kf[a % 3], qf[a], sn);
-        exp_chunk<E0, E1>(w.st, cq, m_use, pw, ls);
-        if constexpr (DMA) dma_at<a, NS>(p, smem, bd, dl, wave, lane);
-      });
-    } else {
-      exp_chunk<0, 16>(w.st, cq, m_use, pw, ls);
+    for (int e = 0; e < 16; ++e) {
+      w.st[e] = fast_exp2(fmaf(w.st[e], cq, -m_use));
+      ls[e & 1] += w.st[e];
+      if (e & 1) w.pw[e >> 1] = pack_bf16x2(w.st[e - 1], w.st[e]);
     }
+    w.l += ls[0] + ls[1];
+    MHA_SLOT_FENCE();
+  }
 
-    // ---- phase B: P V products (+ next sub-tile's scale, mask and max)
+  // Matrix-core half-step: P V of sub-tile i (P in w.pw, V rows at vh) and
+  // S of sub-tile i+1 (K rows at kn / rn) into w.st; the S of a sub-tile
+  // past the wave's last is computed from whatever the slot holds and never
+  // used.
+  static __device__ __forceinline__ void gphase(State& w, uint32_t kn, uint32_t rn,
+                                                const uint32_t (&vh)[C::DV_TILES],
+                                                const QFrag* qf) {
+    constexpr int NS = C::S_STEPS + C::NPV;  // matrix-core slots
+    MHA_SLOT_FENCE();
     bf16x8 pb[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      pb[u] = __builtin_bit_cast(
-          bf16x8, i32x4{(int)pw[4 * u], (int)pw[4 * u + 1], (int)pw[4 * u + 2], (int)pw[4 * u + 3]});
-    float mxp = -INFINITY;
-    bf16x8 vf[3];
-    vf[0] = v_frag(src.vh, 0);
-    vf[1] = v_frag(src.vh, 1);
-    static_for<0, C::NPV>([&](auto bc) {
-      constexpr int b = decltype(bc)::value;
-      if constexpr (b + 2 < C::NPV) vf[(b + 2) % 3] = v_frag(src.vh, b + 2);
-      w.o[b % C::DV_TILES] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          vf[b % 3], pb[b / C::DV_TILES], w.o[b % C::DV_TILES], 0, 0, 0);
-      if constexpr (NEXT) {
+      pb[u] = __builtin_bit_cast(bf16x8, i32x4{(int)w.pw[4 * u], (int)w.pw[4 * u + 1],
+                                               (int)w.pw[4 * u + 2], (int)w.pw[4 * u + 3]});
+    f32x16 sn;
 #pragma unroll
-        for (int e = b * 16 / C::NPV; e < (b + 1) * 16 / C::NPV; ++e)
-          finish_elem(sn, e, src.ks, hf, mxp);
+    for (int r = 0; r < 16; ++r) sn[r] = 0.f;
+    // products alternate between the P V and the S streams while both last
+    static_for<0, NS>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int NPAIR = C::NPV < C::S_STEPS ? C::NPV : C::S_STEPS;
+      constexpr bool PV = k < 2 * NPAIR ? (k % 2 == 0) : (C::NPV > C::S_STEPS);
+      constexpr int idx = k < 2 * NPAIR ? k / 2 : k - NPAIR;
+      if constexpr (PV) {
+        w.o[idx % C::DV_TILES] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            v_frag(vh, idx), pb[idx / C::DV_TILES], w.o[idx % C::DV_TILES], 0, 0, 0);
+      } else {
+        sn = s_mfma(s_frag(kn, rn, idx), qf[idx], sn);
       }
-      if constexpr (DMA) dma_at<(NEXT ? C::S_STEPS : 0) + b, NS>(p, smem, bd, dl, wave, lane);
     });
+    // Slot shape for the machine scheduler: each product's operands are
+    // read two products ahead (not all at the start, which would hold 16
+    // operand fragments in registers at once).
+    static_for<0, NS + 2>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;  // reads for product k, then product k - 2
+      constexpr int NPAIR = C::NPV < C::S_STEPS ? C::NPV : C::S_STEPS;
+      if constexpr (k < NS) {
+        constexpr bool PV = k < 2 * NPAIR ? (k % 2 == 0) : (C::NPV > C::S_STEPS);
+        __builtin_amdgcn_sched_group_barrier(0x100, PV ? 2 : (C::FP8 ? 2 : 1), 0);
+      }
+      if constexpr (k >= 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    });
+    w.st = sn;
     MHA_SLOT_FENCE();
-    w.l += ls[0] + ls[1];
-    if constexpr (NEXT) {
-      w.st = sn;
-      w.mx = half_max(mxp) * cq;
-    }
   }
 
   // ------------------------------------------------------------ kernel body
@@ -665,72 +637,84 @@ struct MfmaKernel {
       w.m = -INFINITY;
       w.l = 0.f;
 
-      // Prologue: batch t of the pipeline is {K_{t+3}, V_{t+2}}; block j
-      // issues batch j.  Batches -3 and -2 ({K_0} and {K_1, V_0}) are waited
-      // for here together with the Q loads (the compiler's own wait for
-      // those could not tell the DMA apart anyway); batch -1 ({K_2, V_1})
-      // goes out after the first S.
-      dma_all(p, smem, block_dma(p, smem, s0, L, g, 0, -1, nblocks), dl, wave, lane);
-      dma_all(p, smem, block_dma(p, smem, s0, L, g, 1, 0, nblocks), dl, wave, lane);
+      // The DMA pipeline: batch t is {K_{t+KLEAD}, V_{t+2}}, and block j
+      // issues batch j.  The prologue issues the batches before block 0:
+      // those needed in block 0 are waited for here together with the Q
+      // loads (the compiler's own wait for those could not tell the DMA
+      // apart anyway); with 4 K slots the last one goes out after the first
+      // S.
+      auto blk = [&](int t) {
+        return block_dma(p, smem, s0, L, g, t + C::KLEAD, t + 2, nblocks);
+      };
+      for (int t = -C::KLEAD; t < (C::KLEAD == 3 ? -1 : 0); ++t)
+        dma_all(p, smem, blk(t), dl, wave, lane);
       wait_vm<0>();
       if (tid == 0) s_item[(it + 1) & 1] = nxt;
       __syncthreads();
-      if (n_sub > 0) {
-        s_tile(opaque(sbase + C::K_OFF + ln.k), opaque(sbase + C::R_OFF + ln.r),
-               reinterpret_cast<const float*>(smem + C::KS_OFF), qf, hf, cq, w);
-        if (n_sub == 1) mask_tile(w, 0, lim, hf, cq);
-      }
-      dma_all(p, smem, block_dma(p, smem, s0, L, g, 2, 1, nblocks), dl, wave, lane);
+      if (n_sub > 0) s_tile(opaque(sbase + C::K_OFF + ln.k), opaque(sbase + C::R_OFF + ln.r), qf, w);
+      if constexpr (C::KLEAD == 3) dma_all(p, smem, blk(-1), dl, wave, lane);
 
-      // Block j: sub-steps 2j (S of keys 32..63 of block j, P V of keys
-      // 0..31) and 2j+1 (S of keys 0..31 of block j+1, P V of keys 32..63);
-      // K_{j+3} and V_{j+2} are requested; at the end K_{j+2} and V_{j+1}
-      // (requested in block j-1) must have landed, then one barrier.
-      auto src_of = [&](int i) {
-        // operands of sub-step i: next sub-tile i+1's K, this sub-tile's V
-        const int jn = (i + 1) >> 1, hn = (i + 1) & 1;
-        const uint32_t ks = sbase + (jn % C::NKS) * C::KSLOT;
-        const uint32_t vs =
-            sbase + C::V_BASE + ((i >> 1) % C::NVS) * C::VSLOT + (i & 1) * 32 * C::V_RB;
-        StepSrc s;
-        s.kn = opaque(ks + C::K_OFF + hn * 32 * C::K_RP + ln.k);
-        s.rn = C::DR > 0 ? opaque(ks + C::R_OFF + hn * 32 * C::R_RP + ln.r) : 0u;
-        s.ks = reinterpret_cast<const float*>(smem + (jn % C::NKS) * C::KSLOT + C::KS_OFF) + 32 * hn;
+      // Per wave the sub-tiles run as alternating half-steps X_0 G_0 X_1
+      // G_1 ...: X_i is sub-tile i's softmax (vector ALU), G_i its P V and
+      // the next sub-tile's S (matrix cores).  Waves w and w + 4 share a
+      // SIMD.  Every wave runs X_{2j} G_{2j} X_{2j+1} G_{2j+1} per block, but
+      // group 1 (waves 4-7) takes the block's barrier before G_{2j+1} and
+      // group 0 after it: between two barriers group 0 runs X G X G and
+      // group 1 G X G X, so on every SIMD one wave's softmax overlaps the
+      // other's products (the ping-pong of the pages' two softmax warp
+      // groups).  Group 1 reads V_j after barrier j, hence 4 V slots.  At
+      // each barrier j, K_{j+2} and V_{j+1} must have landed.
+      const int grp = wave >> 2;
+      constexpr int OPH = C::N_OPS / 2;  // DMA ops issued in the block's first softmax half-step
+      auto xh = [&](auto part, int i, const BlockDma& bd) {
+        constexpr int O0 = decltype(part)::value == 0 ? 0 : OPH;
+        constexpr int O1 = decltype(part)::value == 0 ? OPH : C::N_OPS;
+        if (i < n_sub) {
+          const float* ks = reinterpret_cast<const float*>(
+                                smem + ((i >> 1) % C::NKS) * C::KSLOT + C::KS_OFF) +
+                            32 * (i & 1);
+          xphase<O0, O1>(w, ks, hf, cq, i == n_sub - 1, lim - 32 * i - 4 * hf, p, smem, bd, dl,
+                         wave, lane);
+        } else {
+          static_for<O0, O1>(
+              [&](auto oc) { dma_op<decltype(oc)::value>(p, smem, bd, dl, wave, lane); });
+        }
+      };
+      auto gh = [&](int i) {
+        if (i >= 0 && i < n_sub) {
+          const int jn = (i + 1) >> 1, hn = (i + 1) & 1;
+          const uint32_t ks = sbase + (jn % C::NKS) * C::KSLOT;
+          const uint32_t vs =
+              sbase + C::V_BASE + ((i >> 1) % C::NVS) * C::VSLOT + (i & 1) * 32 * C::V_RB;
+          uint32_t vh[C::DV_TILES];
 #pragma unroll
-        for (int t = 0; t < C::DV_TILES; ++t) s.vh[t] = opaque(vs + ln.v[t]);
-        return s;
+          for (int t = 0; t < C::DV_TILES; ++t) vh[t] = opaque(vs + ln.v[t]);
+          gphase(w, opaque(ks + C::K_OFF + hn * 32 * C::K_RP + ln.k),
+                 C::DR > 0 ? opaque(ks + C::R_OFF + hn * 32 * C::R_RP + ln.r) : 0u, vh, qf);
+        }
       };
-      // end of block j: batch j may stay in flight, batch j-1 must be in
-      auto finish = [&]() { publish<C::N_OPS>(); };
-      auto blk = [&](int j) { return block_dma(p, smem, s0, L, g, j + 3, j + 2, nblocks); };
-      using Y = std::true_type;
-      using N = std::false_type;
-      auto run_step = [&](auto next, auto dma, int i, const BlockDma& bd) {
-        step<decltype(next)::value, decltype(dma)::value>(w, src_of(i), qf, lane, lane32, hf, cq,
-                                                          p, smem, bd, dl, wave);
-        // the sub-tile just computed is the wave's last: mask it
-        if (i + 1 == n_sub - 1) mask_tile(w, 32 * (i + 1), lim, hf, cq);
+      using P0 = std::integral_constant<int, 0>;
+      using P1 = std::integral_constant<int, 1>;
+      auto publish_block = [&]() {
+        if constexpr (C::KLEAD == 3)
+          publish<C::N_OPS>();  // batch j may stay in flight
+        else
+          publish<C::V_DMA>();  // batch j's K part must be in too
       };
-      // A wave's last sub-tile also computes the S of a sub-tile that does
-      // not exist (from whatever its K slot holds); that S is never used,
-      // which costs one sub-tile of S products per wave and item but keeps
-      // a single step body per position in the block.
       for (int j = 0; j < nblocks; ++j) {
         const BlockDma bd = blk(j);
-        const int i0 = 2 * j;
-        if (i0 < n_sub) {
-          run_step(Y{}, Y{}, i0, bd);
-          if (i0 + 1 < n_sub) run_step(Y{}, N{}, i0 + 1, bd);
-        } else {
-          // past this wave's last visible key: keep the workgroup's DMA and
-          // barrier rhythm only
-          dma_all(p, smem, bd, dl, wave, lane);
-        }
-        finish();
+        xh(P0{}, 2 * j, bd);
+        gh(2 * j);
+        xh(P1{}, 2 * j + 1, bd);
+        if (grp == 1) publish_block();
+        gh(2 * j + 1);
+        if (grp == 0) publish_block();
       }
-      // the last batches requested nothing; drain before the rings are
-      // reused for the output staging
+      // the last batches requested nothing; drain, and let group 1 finish
+      // its last products, before the rings are reused for the output
+      // staging
       wait_vm<0>();
+      __syncthreads();
 
       // ---- epilogue
       const float lt = half_sum(w.l);
