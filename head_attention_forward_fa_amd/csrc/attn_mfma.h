@@ -246,11 +246,14 @@ struct MfmaKernel {
   }
 
   // This wave's DMA source offsets (fixed for the kernel: they depend on the
-  // head stride only).
+  // head stride only).  An instruction index past a region's end gets rows
+  // past every block (all lanes out of range, zeros); another wave's k_scale
+  // instruction gets lanes out of range too.
   struct DmaLanes {
     uint32_t k[C::K_DMA];
     uint32_t r[C::R_DMA > 0 ? C::R_DMA : 1];
     uint32_t v[C::V_DMA];
+    uint32_t ks;
   };
   static __device__ __forceinline__ DmaLanes dma_lanes(const AttnParams& p, int wave, int lane) {
     DmaLanes d;
@@ -266,82 +269,97 @@ struct MfmaKernel {
 #pragma unroll
     for (int i = 0; i < C::V_DMA; ++i)
       d.v[i] = dma_v_lane_off<C::V_RB>(wave + C::WAVES * i, lane, Hkv * C::V_RB);
+    d.ks = wave == 0 ? (uint32_t)(lane * Hkv * 4) : 0x80000000u;
+    return d;
+  }
+
+  // Per-item DMA sources: this (sequence, KV head)'s first row of each
+  // tensor, the bytes one block advances, and the range of a full and of the
+  // last block (one row of a block every Hkv rows of [T, Hkv]).
+  struct DmaSrc {
+    const char* k;
+    const char* r;
+    const char* ks;
+    const char* v;
+    uint32_t rows_stride;        // [T, Hkv] rows per block: BN * Hkv
+    uint32_t span_full, span_last;  // [T, Hkv] rows a full / the last block spans
+    int nblocks;
+  };
+  static __device__ __forceinline__ DmaSrc dma_src(const AttnParams& p, int s0, int L, int g,
+                                                  int nblocks) {
+    const uint32_t Hkv = (uint32_t)p.num_kv_heads;
+    const size_t row0 = (size_t)s0 * Hkv + (uint32_t)g;
+    DmaSrc d;
+    d.k = static_cast<const char*>(p.k) + row0 * C::K_RB;
+    d.r = static_cast<const char*>(p.k_rope) + row0 * C::R_RB;
+    d.ks = reinterpret_cast<const char*>(p.k_scale + row0);
+    d.v = static_cast<const char*>(p.v) + row0 * C::V_RB;
+    d.rows_stride = C::BN * Hkv;
+    d.span_full = (C::BN - 1) * Hkv + 1;
+    d.span_last = (uint32_t)(min(L - (nblocks - 1) * C::BN, C::BN) - 1) * Hkv + 1;
+    d.nblocks = nblocks;
     return d;
   }
 
   // One batch of the DMA pipeline: the K side of block kblk and the V of
-  // block vblk (different blocks), as first [T, Hkv] row and row span
-  // (span 0: the block does not exist) and destination slots.
+  // block vblk (different blocks).  A block that does not exist gets empty
+  // ranges and still its own slot, which nobody reads while it is written.
   struct BlockDma {
-    uint32_t krow, vrow;  // [T, Hkv] row index (T * Hkv < 2^32: K alone would pass 512 GB)
-    int kspan, vspan;
-    uint32_t kdst, vdst;           // LDS slot addresses
+    i32x4 k, r, ks, v;       // buffer resources
+    uint32_t kdst, vdst;     // this wave's 1 KiB run in the K / V slot
   };
-  static __device__ __forceinline__ BlockDma block_dma(const AttnParams& p, const char* smem,
-                                                      int s0, int L, int g, int kblk, int vblk,
-                                                      int nblocks) {
-    const int Hkv = p.num_kv_heads;
+  template <int RB>
+  static __device__ __forceinline__ i32x4 block_rsrc(const char* base, const DmaSrc& d, int blk,
+                                                    uint32_t span) {
+    return rsrc_of(base + (size_t)((uint32_t)blk * d.rows_stride) * RB, span * RB);
+  }
+  static __device__ __forceinline__ BlockDma block_dma(const DmaSrc& d, uint32_t sbase, int wave,
+                                                      int kblk, int vblk) {
+    const uint32_t kspan =
+        kblk < d.nblocks - 1 ? d.span_full : (kblk == d.nblocks - 1 ? d.span_last : 0u);
+    const uint32_t vspan = vblk >= 0 && vblk < d.nblocks
+                               ? (vblk < d.nblocks - 1 ? d.span_full : d.span_last)
+                               : 0u;
+    const int kb = kspan ? kblk : 0, vb = vspan ? vblk : 0;  // keep addresses in range
     BlockDma b;
-    const bool kon = kblk >= 0 && kblk < nblocks;
-    const bool von = vblk >= 0 && vblk < nblocks;
-    const int kk = kon ? kblk * C::BN : 0, vk = von ? vblk * C::BN : 0;
-    b.krow = (uint32_t)(s0 + kk) * (uint32_t)Hkv + (uint32_t)g;
-    b.vrow = (uint32_t)(s0 + vk) * (uint32_t)Hkv + (uint32_t)g;
-    b.kspan = kon ? (min(L - kk, C::BN) - 1) * Hkv + 1 : 0;
-    b.vspan = von ? (min(L - vk, C::BN) - 1) * Hkv + 1 : 0;
-    b.kdst = lds_addr_of(smem + (kon ? (kblk % C::NKS) * C::KSLOT : C::JUNK));
-    b.vdst = lds_addr_of(smem + (von ? C::V_BASE + (vblk % C::NVS) * C::VSLOT : C::JUNK));
+    b.k = block_rsrc<C::K_RB>(d.k, d, kb, kspan);
+    if constexpr (C::DR > 0) b.r = block_rsrc<C::R_RB>(d.r, d, kb, kspan);
+    if constexpr (C::FP8) b.ks = block_rsrc<4>(d.ks, d, kb, kspan);
+    b.v = block_rsrc<C::V_RB>(d.v, d, vb, vspan);
+    b.kdst = sbase + (uint32_t)(kblk % C::NKS) * C::KSLOT + 1024u * (uint32_t)wave;
+    b.vdst = sbase + C::V_BASE + (uint32_t)(vblk & (C::NVS - 1)) * C::VSLOT +
+             1024u * (uint32_t)wave;
     return b;
   }
   // DMA op OP of this wave (K nope, K rope, fp8 k_scale, V, in that order).
-  // Branch-free: a padding op gets an empty range and the JUNK destination.
+  // An instruction index past its region's end (for this wave) and another
+  // wave's k_scale instruction write their zeros into the JUNK sink.
   template <int OP>
-  static __device__ __forceinline__ void dma_op(const AttnParams& p, const char* smem,
-                                                const BlockDma& b, const DmaLanes& d, int wave,
-                                                int lane) {
-    const uint32_t junk = lds_addr_of(smem + C::JUNK);
+  static __device__ __forceinline__ void dma_op(const BlockDma& b, const DmaLanes& d,
+                                                uint32_t junk, int wave) {
     if constexpr (OP < C::K_DMA) {
-      const int n = wave + C::WAVES * OP;
-      const bool real = (C::K_INST % C::WAVES == 0 || n < C::K_INST) && b.kspan > 0;
-      dma16(rsrc_of(static_cast<const char*>(p.k) + (size_t)b.krow * C::K_RB,
-                    real ? (uint32_t)b.kspan * C::K_RB : 0u),
-            __builtin_amdgcn_readfirstlane(real ? b.kdst + C::K_OFF + 1024 * n : junk), d.k[OP]);
+      constexpr uint32_t OFF = C::K_OFF + 1024u * C::WAVES * OP;
+      uint32_t m0 = b.kdst + OFF;
+      if constexpr ((OP + 1) * C::WAVES > C::K_INST) m0 = wave + C::WAVES * OP < C::K_INST ? m0 : junk;
+      dma16(b.k, m0, d.k[OP]);
     } else if constexpr (OP < C::K_DMA + C::R_DMA) {
       constexpr int I = OP - C::K_DMA;
-      const int n = wave + C::WAVES * I;
-      const bool real = (C::R_INST % C::WAVES == 0 || n < C::R_INST) && b.kspan > 0;
-      dma16(rsrc_of(static_cast<const char*>(p.k_rope) + (size_t)b.krow * C::R_RB,
-                    real ? (uint32_t)b.kspan * C::R_RB : 0u),
-            __builtin_amdgcn_readfirstlane(real ? b.kdst + C::R_OFF + 1024 * n : junk), d.r[I]);
+      constexpr uint32_t OFF = C::R_OFF + 1024u * C::WAVES * I;
+      uint32_t m0 = b.kdst + OFF;
+      if constexpr ((I + 1) * C::WAVES > C::R_INST) m0 = wave + C::WAVES * I < C::R_INST ? m0 : junk;
+      dma16(b.r, m0, d.r[I]);
     } else if constexpr (OP < C::K_DMA + C::R_DMA + C::KS_DMA) {
-      const bool real = wave == 0 && b.kspan > 0;
-      dma4(rsrc_of(p.k_scale + b.krow, real ? (uint32_t)b.kspan * 4 : 0u),
-           __builtin_amdgcn_readfirstlane(real ? b.kdst + C::KS_OFF : junk),
-           (uint32_t)(lane * p.num_kv_heads * 4));
+      // wave 0's run starts at its slot's k_scale area
+      dma4(b.ks, wave == 0 ? b.kdst + C::KS_OFF : junk, d.ks);
     } else {
       constexpr int I = OP - C::K_DMA - C::R_DMA - C::KS_DMA;
-      const bool real = b.vspan > 0;
-      dma16(rsrc_of(static_cast<const char*>(p.v) + (size_t)b.vrow * C::V_RB,
-                    real ? (uint32_t)b.vspan * C::V_RB : 0u),
-            __builtin_amdgcn_readfirstlane(real ? b.vdst + 1024 * (wave + C::WAVES * I) : junk),
-            d.v[I]);
+      dma16(b.v, b.vdst + 1024u * C::WAVES * I, d.v[I]);
     }
   }
-  static __device__ __forceinline__ void dma_all(const AttnParams& p, const char* smem,
-                                                 const BlockDma& b, const DmaLanes& d, int wave,
-                                                 int lane) {
-    static_for<0, C::N_OPS>(
-        [&](auto oc) { dma_op<decltype(oc)::value>(p, smem, b, d, wave, lane); });
-  }
-  // The ops whose place in a step of NS slots is slot SLOT.
-  template <int SLOT, int NS>
-  static __device__ __forceinline__ void dma_at(const AttnParams& p, const char* smem,
-                                                const BlockDma& b, const DmaLanes& d, int wave,
-                                                int lane) {
-    static_for<0, C::N_OPS>([&](auto oc) {
-      constexpr int OP = decltype(oc)::value;
-      if constexpr (OP * NS / C::N_OPS == SLOT) dma_op<OP>(p, smem, b, d, wave, lane);
-    });
+  template <int OP0, int OP1>
+  static __device__ __forceinline__ void dma_ops(const BlockDma& b, const DmaLanes& d,
+                                                 uint32_t junk, int wave) {
+    static_for<OP0, OP1>([&](auto oc) { dma_op<decltype(oc)::value>(b, d, junk, wave); });
   }
 
   // ------------------------------------------------------------ operands
@@ -451,12 +469,11 @@ struct MfmaKernel {
   // 8(e/4) + 4 hf + e%4 of the sub-tile.
   template <int OP0, int OP1>
   static __device__ __forceinline__ void xphase(State& w, const float* ks, int hf, float cq,
-                                                bool mask, int rel, const AttnParams& p,
-                                                const char* smem, const BlockDma& bd,
-                                                const DmaLanes& dl, int wave, int lane) {
+                                                bool mask, int rel, const BlockDma& bd,
+                                                const DmaLanes& dl, uint32_t junk, int wave) {
     MHA_SLOT_FENCE();
     // this half-step's share of the block's DMA ops
-    static_for<OP0, OP1>([&](auto oc) { dma_op<decltype(oc)::value>(p, smem, bd, dl, wave, lane); });
+    dma_ops<OP0, OP1>(bd, dl, junk, wave);
     float x = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -495,13 +512,20 @@ struct MfmaKernel {
     MHA_SLOT_FENCE();
   }
 
-  // Matrix-core half-step: P V of sub-tile i (P in w.pw, V rows at vh) and
-  // S of sub-tile i+1 (K rows at kn / rn) into w.st; the S of a sub-tile
+  // Matrix-core half-step: P V of sub-tile i (P in w.pw, V rows in half VH
+  // of the V block at vb) and S of sub-tile i+1 (K rows in half KH of the K
+  // block at kb / rb) into w.st; the S of a sub-tile
   // past the wave's last is computed from whatever the slot holds and never
   // used.
-  static __device__ __forceinline__ void gphase(State& w, uint32_t kn, uint32_t rn,
-                                                const uint32_t (&vh)[C::DV_TILES],
+  template <int KH, int VH>
+  static __device__ __forceinline__ void gphase(State& w, uint32_t kb, uint32_t rb,
+                                                const uint32_t (&vb)[C::DV_TILES],
                                                 const QFrag* qf) {
+    // K rows of half KH of the K block, V rows of half VH of the V block
+    const uint32_t kn = kb + KH * 32 * C::K_RP, rn = rb + KH * 32 * C::R_RP;
+    uint32_t vh[C::DV_TILES];
+#pragma unroll
+    for (int t = 0; t < C::DV_TILES; ++t) vh[t] = vb[t] + VH * 32 * C::V_RB;
     constexpr int NS = C::S_STEPS + C::NPV;  // matrix-core slots
     MHA_SLOT_FENCE();
     bf16x8 pb[2];
@@ -557,6 +581,7 @@ struct MfmaKernel {
     const DmaLanes dl = dma_lanes(p, wave, lane);
     const Lanes ln = lanes_of(lane);
     const uint32_t sbase = lds_addr_of(smem);
+    const uint32_t junk = sbase + C::JUNK;
 
     // wave 0 runs the work-item source; the next item's table entry is read
     // while the current item's first blocks load and published at the first
@@ -643,16 +668,15 @@ struct MfmaKernel {
       // loads (the compiler's own wait for those could not tell the DMA
       // apart anyway); with 4 K slots the last one goes out after the first
       // S.
-      auto blk = [&](int t) {
-        return block_dma(p, smem, s0, L, g, t + C::KLEAD, t + 2, nblocks);
-      };
+      const DmaSrc dsrc = dma_src(p, s0, L, g, nblocks);
+      auto blk = [&](int t) { return block_dma(dsrc, sbase, wave, t + C::KLEAD, t + 2); };
       for (int t = -C::KLEAD; t < (C::KLEAD == 3 ? -1 : 0); ++t)
-        dma_all(p, smem, blk(t), dl, wave, lane);
+        dma_ops<0, C::N_OPS>(blk(t), dl, junk, wave);
       wait_vm<0>();
       if (tid == 0) s_item[(it + 1) & 1] = nxt;
       __syncthreads();
       if (n_sub > 0) s_tile(opaque(sbase + C::K_OFF + ln.k), opaque(sbase + C::R_OFF + ln.r), qf, w);
-      if constexpr (C::KLEAD == 3) dma_all(p, smem, blk(-1), dl, wave, lane);
+      if constexpr (C::KLEAD == 3) dma_ops<0, C::N_OPS>(blk(-1), dl, junk, wave);
 
       // Per wave the sub-tiles run as alternating half-steps X_0 G_0 X_1
       // G_1 ...: X_i is sub-tile i's softmax (vector ALU), G_i its P V and
@@ -666,31 +690,31 @@ struct MfmaKernel {
       // each barrier j, K_{j+2} and V_{j+1} must have landed.
       const int grp = wave >> 2;
       constexpr int OPH = C::N_OPS / 2;  // DMA ops issued in the block's first softmax half-step
-      auto xh = [&](auto part, int i, const BlockDma& bd) {
-        constexpr int O0 = decltype(part)::value == 0 ? 0 : OPH;
-        constexpr int O1 = decltype(part)::value == 0 ? OPH : C::N_OPS;
+      // softmax half-step of sub-tile i = 2j + H (k_scale from K block j)
+      auto xh = [&](auto part, int i, int j, const BlockDma& bd) {
+        constexpr int H = decltype(part)::value;
+        constexpr int O0 = H == 0 ? 0 : OPH;
+        constexpr int O1 = H == 0 ? OPH : C::N_OPS;
         if (i < n_sub) {
-          const float* ks = reinterpret_cast<const float*>(
-                                smem + ((i >> 1) % C::NKS) * C::KSLOT + C::KS_OFF) +
-                            32 * (i & 1);
-          xphase<O0, O1>(w, ks, hf, cq, i == n_sub - 1, lim - 32 * i - 4 * hf, p, smem, bd, dl,
-                         wave, lane);
+          const float* ks =
+              reinterpret_cast<const float*>(smem + (j % C::NKS) * C::KSLOT + C::KS_OFF) + 32 * H;
+          xphase<O0, O1>(w, ks, hf, cq, i == n_sub - 1, lim - 32 * i - 4 * hf, bd, dl, junk, wave);
         } else {
-          static_for<O0, O1>(
-              [&](auto oc) { dma_op<decltype(oc)::value>(p, smem, bd, dl, wave, lane); });
+          dma_ops<O0, O1>(bd, dl, junk, wave);
         }
       };
-      auto gh = [&](int i) {
+      // product half-step of sub-tile i: V of block j (half VH), K of block
+      // jk (half KH)
+      auto gh = [&](auto kh, auto vh_, int i, int j, int jk) {
         if (i >= 0 && i < n_sub) {
-          const int jn = (i + 1) >> 1, hn = (i + 1) & 1;
-          const uint32_t ks = sbase + (jn % C::NKS) * C::KSLOT;
-          const uint32_t vs =
-              sbase + C::V_BASE + ((i >> 1) % C::NVS) * C::VSLOT + (i & 1) * 32 * C::V_RB;
-          uint32_t vh[C::DV_TILES];
+          const uint32_t ks = sbase + (uint32_t)(jk % C::NKS) * C::KSLOT;
+          const uint32_t vs = sbase + C::V_BASE + (uint32_t)(j & (C::NVS - 1)) * C::VSLOT;
+          uint32_t vb[C::DV_TILES];
 #pragma unroll
-          for (int t = 0; t < C::DV_TILES; ++t) vh[t] = opaque(vs + ln.v[t]);
-          gphase(w, opaque(ks + C::K_OFF + hn * 32 * C::K_RP + ln.k),
-                 C::DR > 0 ? opaque(ks + C::R_OFF + hn * 32 * C::R_RP + ln.r) : 0u, vh, qf);
+          for (int t = 0; t < C::DV_TILES; ++t) vb[t] = opaque(vs + ln.v[t]);
+          gphase<decltype(kh)::value, decltype(vh_)::value>(
+              w, opaque(ks + C::K_OFF + ln.k), C::DR > 0 ? opaque(ks + C::R_OFF + ln.r) : 0u, vb,
+              qf);
         }
       };
       using P0 = std::integral_constant<int, 0>;
@@ -703,11 +727,11 @@ struct MfmaKernel {
       };
       for (int j = 0; j < nblocks; ++j) {
         const BlockDma bd = blk(j);
-        xh(P0{}, 2 * j, bd);
-        gh(2 * j);
-        xh(P1{}, 2 * j + 1, bd);
+        xh(P0{}, 2 * j, j, bd);
+        gh(P1{}, P0{}, 2 * j, j, j);
+        xh(P1{}, 2 * j + 1, j, bd);
         if (grp == 1) publish_block();
-        gh(2 * j + 1);
+        gh(P0{}, P1{}, 2 * j + 1, j, j + 1);
         if (grp == 0) publish_block();
       }
       // the last batches requested nothing; drain, and let group 1 finish
