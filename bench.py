@@ -10,19 +10,33 @@ prefill, B=4, H=32, S=4096, D=128.  Prints one JSON line.
 value      attention TFLOP/s = metric FLOPs (4*B*H*S^2*D, halved for causal)
            / mean step time over the K timed steps;
 roofline   the attention kernel against the dense MFMA peak of its dtype:
-           achieved = metric FLOPs per launch / mean launch duration (HIP
-           events on the launch stream around each call, so it includes the
-           few-microsecond prepass);
+           achieved = metric FLOPs per launch / mean duration of the attention
+           kernel itself (HIP events that the library records on the launch
+           stream right before and after the kernel, mha_fwd_set_kernel_events;
+           the scheduler prepass is outside them); traffic = HBM bytes per
+           launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary committed
+           under profiles/ for this workload, scaled by the plain-copy
+           calibration recorded there, or null when the kernel sources have
+           changed since those counters were taken;
 cpu_baseline  the float64 CPU oracle on a bounded sample of the same
            workload: whole (sequence, head) pairs, as many as fit in about
            10 s, rated with the same metric FLOPs.
+
+    python bench.py --summarize-profile DIR --workload NAME
+writes profiles/<kernel>_<workload>.md from the rocprofv3 output under DIR
+(trace/, pmcA/, pmcB/, pmcC/ = FETCH_SIZE, pmcD/ = WRITE_SIZE, copy_fetch/,
+copy_write/ = the same two counters on --copy-probe-mib 1024).
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -37,6 +51,68 @@ DEFAULT_WORKLOAD = "bf16_causal_b4_h32_s4096_d128"
 METRIC = "attention fwd TFLOP/s (4·B·H·Sq·Sk·D, causal halved) and % of MFMA peak"
 # MI355X dense matrix peaks (TFLOP/s) by the dtype of the products
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+
+
+KERNEL = "attn_fwd_mfma_kernel"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+COPY_PROBE_MIB = 1024
+
+
+def kernel_sources_sha256() -> str:
+    """Hash of the library sources: a traffic figure is valid for these only."""
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "head_attention_forward_fa_amd", "csrc")
+    for f in sorted(os.listdir(src)):
+        if f.endswith((".h", ".hip", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(src, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def profile_path(workload: str) -> str:
+    return os.path.join(PROFILE_DIR, f"{KERNEL}_{workload}.md")
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch recorded for the current sources, else None."""
+    path = profile_path(workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"sources_sha256=(\w+)\s+hbm_bytes_per_launch=([0-9.e+]+)", text)
+    if not m or m.group(1) != kernel_sources_sha256():
+        return None
+    return float(m.group(2))
+
+
+class HipEvents:
+    """Timing events of the HIP runtime the process already uses (the same
+    library instance that PyTorch and libmha_fwd.so share)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        if self.hip.hipEventCreate(self.ct.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
 
 
 def peak_for(inp) -> float:
@@ -101,6 +177,138 @@ def cpu_baseline(inp, budget_s: float = 10.0):
     }
 
 
+def _csv_rows(d: str, suffix: str):
+    files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _pmc_per_dispatch(d: str, kernel_substr: str):
+    """Mean per-dispatch value of every counter of the matching kernel."""
+    acc = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if kernel_substr in r["Kernel_Name"]:
+            acc.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            acc[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {c: sum(v.values()) / len(v) for c, v in acc.items()}
+
+
+def summarize_profile(prof: str, workload: str) -> str:
+    """profiles/<kernel>_<workload>.md from the rocprofv3 runs under prof."""
+    inp = mi.workload(workload)
+    stats = _csv_rows(os.path.join(prof, "trace"), "kernel_stats.csv")
+    krow = next(r for r in stats if KERNEL in r["Name"])
+    prow = [r for r in stats if "sched_prepass" in r["Name"]]
+    avg_ns = float(krow["AverageNs"])
+    a = _pmc_per_dispatch(os.path.join(prof, "pmcA"), KERNEL)
+    b = _pmc_per_dispatch(os.path.join(prof, "pmcB"), KERNEL)
+    fetch = _pmc_per_dispatch(os.path.join(prof, "pmcC"), KERNEL)["FETCH_SIZE"]
+    write = _pmc_per_dispatch(os.path.join(prof, "pmcD"), KERNEL)["WRITE_SIZE"]
+    # dst.copy_(src) of one contiguous buffer is the runtime's copyBuffer kernel
+    cf = _pmc_per_dispatch(os.path.join(prof, "copy_fetch"), "copyBuffer")["FETCH_SIZE"]
+    cw = _pmc_per_dispatch(os.path.join(prof, "copy_write"), "copyBuffer")["WRITE_SIZE"]
+    copy_kib = COPY_PROBE_MIB * 1024.0
+    f_fetch, f_write = copy_kib / cf, copy_kib / cw
+    hbm = (fetch * f_fetch + write * f_write) * 1024.0
+    flops = mi.attention_flops(inp)
+    peak = peak_for(inp)
+    algo = algorithmic_bytes(inp)
+    mfma_busy = a.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan"))
+    busy_cu = b.get("SQ_BUSY_CU_CYCLES", float("nan"))
+    gui = a.get("GRBM_GUI_ACTIVE", float("nan"))
+    bank = b.get("SQ_LDS_BANK_CONFLICT", float("nan"))
+    lds_active = b.get("SQ_LDS_IDX_ACTIVE", float("nan"))
+    bench_cmd = f"python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --workload {workload}"
+    lines = [
+        f"# {KERNEL} on {workload}",
+        "",
+        "rocprofv3 on one MI355X (gfx950), launched from the repository root after",
+        "`cd /tmp && export TMPDIR=/tmp`; R is the repository root:",
+        "",
+        "```",
+        f"rocprofv3 --kernel-trace --stats -f csv -T -d gpurun_out/prof/trace -o run -- {bench_cmd}",
+        f"rocprofv3 --pmc SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
+        f"SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_LDS GRBM_GUI_ACTIVE -f csv -T "
+        f"-d gpurun_out/prof/pmcA -o run -- {bench_cmd}",
+        f"rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAIT_ANY "
+        f"SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_LDS SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE "
+        f"-f csv -T -d gpurun_out/prof/pmcB -o run -- {bench_cmd}",
+        f"rocprofv3 --pmc FETCH_SIZE -f csv -T -d gpurun_out/prof/pmcC -o run -- {bench_cmd}",
+        f"rocprofv3 --pmc WRITE_SIZE -f csv -T -d gpurun_out/prof/pmcD -o run -- {bench_cmd}",
+        f"rocprofv3 --pmc FETCH_SIZE -f csv -T -d gpurun_out/prof/copy_fetch -o run -- "
+        f"python3 bench.py --copy-probe-mib {COPY_PROBE_MIB}",
+        f"rocprofv3 --pmc WRITE_SIZE -f csv -T -d gpurun_out/prof/copy_write -o run -- "
+        f"python3 bench.py --copy-probe-mib {COPY_PROBE_MIB}",
+        f"python3 bench.py --summarize-profile gpurun_out/prof --workload {workload}",
+        "```",
+        "",
+        "## Kernel trace (stats)",
+        "",
+        "| kernel | calls | average ns | min ns | max ns |",
+        "|---|---|---|---|---|",
+        f"| {KERNEL} | {krow['Calls']} | {avg_ns:.0f} | {krow['MinNs']} | {krow['MaxNs']} |",
+    ]
+    for r in prow:
+        lines.append(f"| sched_prepass_kernel | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                     f"{r['MinNs']} | {r['MaxNs']} |")
+    lines += [
+        "",
+        f"Attention TFLOP/s at the trace average: {flops / (avg_ns * 1e-9) / 1e12:.1f} "
+        f"({100 * flops / (avg_ns * 1e-9) / 1e12 / peak:.1f}% of {peak:.0f}).",
+        "",
+        "## Counters (per dispatch of the attention kernel, mean)",
+        "",
+        "| counter | value |",
+        "|---|---|",
+    ]
+    for k2, v in sorted({**a, **b}.items()):
+        lines.append(f"| {k2} | {v:.4g} |")
+    lines += [
+        f"| FETCH_SIZE (KiB) | {fetch:.6g} |",
+        f"| WRITE_SIZE (KiB) | {write:.6g} |",
+        "",
+        f"MFMA busy per SIMD: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs) "
+        f"= {mfma_busy / (1024 * gui / 8):.3f} (GRBM_GUI_ACTIVE adds up the 8 XCDs; "
+        f"{gui / 8 / (avg_ns * 1e-9) / 1e9:.2f} GHz effective clock over the trace average); "
+        f"LDS bank conflicts: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE = {bank / lds_active:.4f}.",
+        "",
+        "## HBM traffic",
+        "",
+        f"Plain copy of {COPY_PROBE_MIB} MiB (device-to-device copyBuffer): FETCH_SIZE reads "
+        f"{cf:.6g} KiB and WRITE_SIZE {cw:.6g} KiB per dispatch, so the scale factors are "
+        f"{f_fetch:.4f} (fetch) and {f_write:.4f} (write).",
+        "",
+        f"Attention kernel: {fetch:.6g} KiB x {f_fetch:.4f} read + {write:.6g} KiB x "
+        f"{f_write:.4f} written = {hbm / 1e6:.1f} MB per launch; algorithmic bytes "
+        f"{algo / 1e6:.1f} MB (ratio {hbm / algo:.3f}); {hbm / (avg_ns * 1e-9) / 1e9:.0f} GB/s.",
+        "",
+        f"traffic: sources_sha256={kernel_sources_sha256()} hbm_bytes_per_launch={hbm:.6e}",
+        "",
+    ]
+    os.makedirs(PROFILE_DIR, exist_ok=True)
+    out = profile_path(workload)
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    return out
+
+
+def algorithmic_bytes(inp) -> float:
+    """Compulsory HBM bytes of one launch: read Q (+rope, +scales), K, V once;
+    write O and LSE once."""
+    T, Hq, Hkv = inp.total_tokens, inp.num_heads, inp.num_kv_heads
+    eqk = {"f32": 4, "bf16": 2, "fp8": 1}[inp.dtype]
+    ev = 4 if inp.dtype == "f32" else 2
+    b = T * Hq * inp.head_dim_nope * eqk + T * Hkv * inp.head_dim_nope * eqk
+    b += T * (Hq + Hkv) * inp.head_dim_rope * 2
+    b += T * Hkv * inp.v_dim * ev
+    if inp.dtype == "fp8":
+        b += T * (Hq + Hkv) * 4
+    b += T * Hq * inp.v_dim * ev + T * Hq * 4
+    return float(b)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,7 +320,12 @@ def main(argv=None):
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (five "
                          "times), to calibrate HBM byte counters against a known size")
+    ap.add_argument("--summarize-profile", default=None,
+                    help="write the profiles/ summary from rocprofv3 output under this directory")
     a = ap.parse_args(argv)
+    if a.summarize_profile:
+        print(summarize_profile(a.summarize_profile, a.workload))
+        return 0
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}): this path has no "
               "multi-GPU mode", file=sys.stderr)
@@ -122,7 +335,7 @@ def main(argv=None):
     from head_attention_forward_fa_amd import mha_fwd
     from head_attention_forward_fa_amd import _native
 
-    _native.load()  # fail loudly if the HIP library is missing
+    lib = _native.load()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if a.copy_probe_mib:
@@ -171,30 +384,34 @@ def main(argv=None):
         print("[bench] non-finite output", file=sys.stderr)
         return 1
 
+    hip = HipEvents()
+    kev = [(hip.create(), hip.create()) for _ in range(a.steps)]
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(a.steps)]
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_all0.record(stream)
     for i in range(a.steps):
-        ev[i][0].record(stream)
+        _native.check(lib.mha_fwd_set_kernel_events(kev[i][0], kev[i][1]))
         step()
-        ev[i][1].record(stream)
     t_all1.record(stream)
+    _native.check(lib.mha_fwd_set_kernel_events(None, None))
     torch.cuda.synchronize()
     total_ms = t_all0.elapsed_time(t_all1)
-    launch_ms = [s.elapsed_time(e) for s, e in ev]
+    kernel_ms = [hip.elapsed_ms(s0, s1) for s0, s1 in kev]
+    for s0, s1 in kev:
+        hip.destroy(s0)
+        hip.destroy(s1)
     ms_per_step = total_ms / a.steps
-    kernel_ms = float(np.mean(launch_ms))
+    kmean = float(np.mean(kernel_ms))
 
     flops = mi.attention_flops(inp)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    achieved = flops / (kmean * 1e-3) / 1e12
     peak = peak_for(inp)
-    print(f"[bench] {ms_per_step * 1e3:.1f} us/step, launch mean {kernel_ms * 1e3:.1f} us "
-          f"(min {min(launch_ms) * 1e3:.1f}), {value:.1f} TFLOP/s, {100 * achieved / peak:.1f}% "
+    traffic = traffic_from_profile(inp.name)
+    print(f"[bench] {ms_per_step * 1e3:.1f} us/step, attention kernel mean {kmean * 1e3:.1f} us "
+          f"(min {min(kernel_ms) * 1e3:.1f}), {value:.1f} TFLOP/s, {100 * achieved / peak:.1f}% "
           f"of {peak:.0f}", file=sys.stderr, flush=True)
 
     cpu = None
@@ -234,7 +451,7 @@ def main(argv=None):
             "peak": round(peak, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else round(traffic),
         },
         "cpu_baseline": cpu,
     }

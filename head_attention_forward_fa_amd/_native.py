@@ -22,7 +22,7 @@ MHA_ERR_UNSUPPORTED = 2
 MHA_ERR_HIP = 3
 
 EXPORTS = ("mha_fwd", "mha_fwd_last_error", "mha_fwd_supported", "mha_fwd_kernel_info",
-           "mha_sched_visit")
+           "mha_fwd_set_kernel_events", "mha_sched_visit")
 
 _lib = None
 
@@ -59,6 +59,8 @@ def load() -> ctypes.CDLL:
     ip = ctypes.POINTER(ctypes.c_int32)
     lib.mha_fwd_kernel_info.argtypes = [i32, i32, i32, i32, ip, ip, ip, ip]
     lib.mha_fwd_kernel_info.restype = ctypes.c_int
+    lib.mha_fwd_set_kernel_events.argtypes = [vp, vp]
+    lib.mha_fwd_set_kernel_events.restype = ctypes.c_int
     lib.mha_sched_visit.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.mha_sched_visit.restype = ctypes.c_int
     _lib = lib

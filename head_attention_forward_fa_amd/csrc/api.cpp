@@ -33,6 +33,10 @@ const Variant* find_variant(int dtype, int dn, int dr, int dv) {
 namespace {
 
 thread_local std::string g_err;
+// measurement hook (mha_fwd_set_kernel_events): events recorded around the
+// attention kernel of each mha_fwd call made by this host thread
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
 
 int fail(int code, const std::string& msg) {
   g_err = msg;
@@ -213,8 +217,25 @@ int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   long long grid = (long long)cu_count(dev) * var->blocks_per_cu();
   if (grid > plan.capacity) grid = plan.capacity;
   if (grid < 1) grid = 1;
+  if (g_ev_start) {
+    e = hipEventRecord(g_ev_start, s);
+    if (e != hipSuccess) return fail_hip(e, "hipEventRecord (start)");
+  }
   e = var->launch(p, (int)grid, s);
   if (e != hipSuccess) return fail_hip(e, "attention kernel launch");
+  if (g_ev_stop) {
+    e = hipEventRecord(g_ev_stop, s);
+    if (e != hipSuccess) return fail_hip(e, "hipEventRecord (stop)");
+  }
+  return MHA_OK;
+}
+
+int mha_fwd_set_kernel_events(void* start_event, void* stop_event) {
+  g_err.clear();
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(MHA_ERR_INVALID_ARG, "start_event and stop_event must both be given or both NULL");
+  g_ev_start = static_cast<hipEvent_t>(start_event);
+  g_ev_stop = static_cast<hipEvent_t>(stop_event);
   return MHA_OK;
 }
 

@@ -143,6 +143,17 @@ int mha_fwd_kernel_info(int32_t dtype, int32_t head_dim_nope, int32_t head_dim_r
                         int32_t* grid, int32_t* lds_bytes);
 
 /*
+ * Measurement hook.  Registers two hipEvent_t handles (created by the
+ * caller, who keeps ownership) that every following mha_fwd call made by the
+ * same host thread records on its stream immediately before and after the
+ * attention kernel, so that the kernel's own duration can be read without a
+ * profiler (the scheduler prepass that precedes it is outside the pair).
+ * NULL, NULL switches the hook off; exactly one NULL is MHA_ERR_INVALID_ARG.
+ * A call whose outputs are empty (max_seqlen == 0) records nothing.
+ */
+int mha_fwd_set_kernel_events(void* start_event, void* stop_event);
+
+/*
  * mha_sched_visit -- diagnostic for the persistent tile scheduler
  * (MHATileScheduler: "maps work tiles to thread blocks, advances the per-CTA
  * state through the work grid").  Builds the work table exactly as mha_fwd

@@ -105,6 +105,13 @@ def test_sched_visit_validation():
     assert lib.mha_sched_visit(FAKE, 1, 0, 4, 2, 1, 256, 0, FAKE, None) == nat.MHA_OK
 
 
+def test_set_kernel_events_validation():
+    lib = nat.load()
+    assert lib.mha_fwd_set_kernel_events(FAKE, None) == nat.MHA_ERR_INVALID_ARG
+    assert lib.mha_fwd_set_kernel_events(None, FAKE) == nat.MHA_ERR_INVALID_ARG
+    assert lib.mha_fwd_set_kernel_events(None, None) == nat.MHA_OK
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     from head_attention_forward_fa_amd import mha_fwd

@@ -106,6 +106,31 @@ def test_repeat_calls_are_bitwise_identical():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_kernel_events_bracket_the_attention_kernel():
+    import ctypes
+    from head_attention_forward_fa_amd import _native
+    lib = _native.load()
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    inp = mi.make_inputs(dtype="bf16", seqlens=[700], num_heads=4, num_kv_heads=4,
+                         head_dim_nope=128, v_dim=128, causal=True, seed=6)
+    t = device_tensors(inp)
+    torch.cuda.synchronize()
+    _native.check(lib.mha_fwd_set_kernel_events(ev[0], ev[1]))
+    try:
+        run_gpu(inp, tensors=t)
+    finally:
+        _native.check(lib.mha_fwd_set_kernel_events(None, None))
+    torch.cuda.synchronize()
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+    assert 0.0 < ms.value < 1000.0
+    for e in ev:
+        hip.hipEventDestroy(e)
+
+
 def test_all_sequences_empty_and_zero_max_seqlen():
     from head_attention_forward_fa_amd import mha_fwd
     dev = "cuda:0"
