@@ -111,19 +111,22 @@ struct MfmaCfg {
   static constexpr int S_STEPS = QK_STEPS + ROPE_STEPS;  // S products per sub-tile
   static constexpr int DV_TILES = DV / 32;
   static constexpr int NPV = 2 * DV_TILES;  // P V products per sub-tile
-  // 1 KiB DMA instructions per block and region; wave w issues instructions
-  // w, w + WAVES, ... of each region (the fp8 k_scale: wave 0, one dword per
-  // lane).  Every wave issues the same N_OPS instructions per block: the
+  static constexpr int G_AHEAD = 2;         // products between an operand read and its use
+  // 1 KiB DMA instructions per block and region.  The waves of group 0
+  // (DW of them, one per SIMD) issue them: wave w takes instructions w,
+  // w + DW, ... of each region (the fp8 k_scale: wave 0, one dword per
+  // lane).  Each of them issues the same N_OPS instructions per block: the
   // ones past a region's end, another wave's k_scale and those of a block
   // that does not exist read nothing (empty buffer range) and land in the
   // JUNK sink, so one vmcnt(N_OPS) wait fits every wave and every block.
+  static constexpr int DW = WAVES / 2;
   static constexpr int K_INST = BN * K_RP / 1024;
   static constexpr int R_INST = BN * R_RP / 1024;
   static constexpr int V_INST = BN * V_RB / 1024;
-  static constexpr int K_DMA = (K_INST + WAVES - 1) / WAVES;
-  static constexpr int R_DMA = (R_INST + WAVES - 1) / WAVES;
+  static constexpr int K_DMA = (K_INST + DW - 1) / DW;
+  static constexpr int R_DMA = (R_INST + DW - 1) / DW;
   static constexpr int KS_DMA = FP8 ? 1 : 0;
-  static constexpr int V_DMA = V_INST / WAVES;
+  static constexpr int V_DMA = V_INST / DW;
   static constexpr int N_OPS = K_DMA + R_DMA + KS_DMA + V_DMA;
 
   static_assert(!FP8 || DR == 0, "fp8 Q/K carry no rope part");
@@ -133,7 +136,7 @@ struct MfmaCfg {
   static_assert(K_INST * 1024 == BN * K_RP && R_INST * 1024 == BN * R_RP &&
                     V_INST * 1024 == BN * V_RB,
                 "regions are whole KiB");
-  static_assert(V_DMA * WAVES == V_INST && V_DMA >= 1, "V DMA splits evenly over the waves");
+  static_assert(V_DMA * DW == V_INST && V_DMA >= 1, "V DMA splits evenly over the waves");
   static_assert(N_OPS <= 15, "vmcnt immediates");
   static_assert(V_BASE % 256 == 0 && VSLOT % 256 == 0, "V rows keep 256-byte alignment");
   static_assert(WAVES * 32 * O_ROW <= LDS, "epilogue staging must fit in the rings");
@@ -260,15 +263,15 @@ struct MfmaKernel {
     const int Hkv = p.num_kv_heads;
 #pragma unroll
     for (int i = 0; i < C::K_DMA; ++i)
-      d.k[i] = dma_k_lane_off<C::K_RB>(wave + C::WAVES * i, lane, Hkv * C::K_RB);
+      d.k[i] = dma_k_lane_off<C::K_RB>(wave + C::DW * i, lane, Hkv * C::K_RB);
     if constexpr (C::R_DMA > 0) {
 #pragma unroll
       for (int i = 0; i < C::R_DMA; ++i)
-        d.r[i] = dma_k_lane_off<C::R_RB>(wave + C::WAVES * i, lane, Hkv * C::R_RB);
+        d.r[i] = dma_k_lane_off<C::R_RB>(wave + C::DW * i, lane, Hkv * C::R_RB);
     }
 #pragma unroll
     for (int i = 0; i < C::V_DMA; ++i)
-      d.v[i] = dma_v_lane_off<C::V_RB>(wave + C::WAVES * i, lane, Hkv * C::V_RB);
+      d.v[i] = dma_v_lane_off<C::V_RB>(wave + C::DW * i, lane, Hkv * C::V_RB);
     d.ks = wave == 0 ? (uint32_t)(lane * Hkv * 4) : 0x80000000u;
     return d;
   }
@@ -338,22 +341,22 @@ struct MfmaKernel {
   static __device__ __forceinline__ void dma_op(const BlockDma& b, const DmaLanes& d,
                                                 uint32_t junk, int wave) {
     if constexpr (OP < C::K_DMA) {
-      constexpr uint32_t OFF = C::K_OFF + 1024u * C::WAVES * OP;
+      constexpr uint32_t OFF = C::K_OFF + 1024u * C::DW * OP;
       uint32_t m0 = b.kdst + OFF;
-      if constexpr ((OP + 1) * C::WAVES > C::K_INST) m0 = wave + C::WAVES * OP < C::K_INST ? m0 : junk;
+      if constexpr ((OP + 1) * C::DW > C::K_INST) m0 = wave + C::DW * OP < C::K_INST ? m0 : junk;
       dma16(b.k, m0, d.k[OP]);
     } else if constexpr (OP < C::K_DMA + C::R_DMA) {
       constexpr int I = OP - C::K_DMA;
-      constexpr uint32_t OFF = C::R_OFF + 1024u * C::WAVES * I;
+      constexpr uint32_t OFF = C::R_OFF + 1024u * C::DW * I;
       uint32_t m0 = b.kdst + OFF;
-      if constexpr ((I + 1) * C::WAVES > C::R_INST) m0 = wave + C::WAVES * I < C::R_INST ? m0 : junk;
+      if constexpr ((I + 1) * C::DW > C::R_INST) m0 = wave + C::DW * I < C::R_INST ? m0 : junk;
       dma16(b.r, m0, d.r[I]);
     } else if constexpr (OP < C::K_DMA + C::R_DMA + C::KS_DMA) {
       // wave 0's run starts at its slot's k_scale area
       dma4(b.ks, wave == 0 ? b.kdst + C::KS_OFF : junk, d.ks);
     } else {
       constexpr int I = OP - C::K_DMA - C::R_DMA - C::KS_DMA;
-      dma16(b.v, b.vdst + 1024u * C::WAVES * I, d.v[I]);
+      dma16(b.v, b.vdst + 1024u * C::DW * I, d.v[I]);
     }
   }
   template <int OP0, int OP1>
@@ -467,7 +470,7 @@ struct MfmaKernel {
   // numbering hidden), row max, lazy correction of O and l, exponentials,
   // row sums and the bf16 packing of P into w.pw.  Element e of a lane is key
   // 8(e/4) + 4 hf + e%4 of the sub-tile.
-  template <int OP0, int OP1>
+  template <int OP0, int OP1, bool MAYMASK>
   static __device__ __forceinline__ void xphase(State& w, const float* ks, int hf, float cq,
                                                 bool mask, int rel, const BlockDma& bd,
                                                 const DmaLanes& dl, uint32_t junk, int wave) {
@@ -480,7 +483,7 @@ struct MfmaKernel {
       if constexpr (C::FP8) w.st[e] *= ks[8 * (e >> 2) + 4 * hf + (e & 3)];
       x = fmaxf(x, w.st[e]);
     }
-    if (mask) {
+    if (MAYMASK && mask) {
       x = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -550,16 +553,17 @@ struct MfmaKernel {
       }
     });
     // Slot shape for the machine scheduler: each product's operands are
-    // read two products ahead (not all at the start, which would hold 16
+    // read G_AHEAD products ahead (not all at the start, which would hold 16
     // operand fragments in registers at once).
-    static_for<0, NS + 2>([&](auto kc) {
-      constexpr int k = decltype(kc)::value;  // reads for product k, then product k - 2
+    constexpr int RA = C::G_AHEAD;
+    static_for<0, NS + RA>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;  // reads for product k, then product k - RA
       constexpr int NPAIR = C::NPV < C::S_STEPS ? C::NPV : C::S_STEPS;
       if constexpr (k < NS) {
         constexpr bool PV = k < 2 * NPAIR ? (k % 2 == 0) : (C::NPV > C::S_STEPS);
         __builtin_amdgcn_sched_group_barrier(0x100, PV ? 2 : (C::FP8 ? 2 : 1), 0);
       }
-      if constexpr (k >= 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if constexpr (k >= RA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     });
     w.st = sn;
     MHA_SLOT_FENCE();
@@ -668,15 +672,18 @@ struct MfmaKernel {
       // loads (the compiler's own wait for those could not tell the DMA
       // apart anyway); with 4 K slots the last one goes out after the first
       // S.
+      const int grp = wave >> 2;  // group 0 issues the DMA
       const DmaSrc dsrc = dma_src(p, s0, L, g, nblocks);
       auto blk = [&](int t) { return block_dma(dsrc, sbase, wave, t + C::KLEAD, t + 2); };
-      for (int t = -C::KLEAD; t < (C::KLEAD == 3 ? -1 : 0); ++t)
-        dma_ops<0, C::N_OPS>(blk(t), dl, junk, wave);
+      if (grp == 0)
+        for (int t = -C::KLEAD; t < (C::KLEAD == 3 ? -1 : 0); ++t)
+          dma_ops<0, C::N_OPS>(blk(t), dl, junk, wave);
       wait_vm<0>();
       if (tid == 0) s_item[(it + 1) & 1] = nxt;
       __syncthreads();
       if (n_sub > 0) s_tile(opaque(sbase + C::K_OFF + ln.k), opaque(sbase + C::R_OFF + ln.r), qf, w);
-      if constexpr (C::KLEAD == 3) dma_ops<0, C::N_OPS>(blk(-1), dl, junk, wave);
+      if constexpr (C::KLEAD == 3)
+        if (grp == 0) dma_ops<0, C::N_OPS>(blk(-1), dl, junk, wave);
 
       // Per wave the sub-tiles run as alternating half-steps X_0 G_0 X_1
       // G_1 ...: X_i is sub-tile i's softmax (vector ALU), G_i its P V and
@@ -688,25 +695,28 @@ struct MfmaKernel {
       // other's products (the ping-pong of the pages' two softmax warp
       // groups).  Group 1 reads V_j after barrier j, hence 4 V slots.  At
       // each barrier j, K_{j+2} and V_{j+1} must have landed.
-      const int grp = wave >> 2;
       constexpr int OPH = C::N_OPS / 2;  // DMA ops issued in the block's first softmax half-step
-      // softmax half-step of sub-tile i = 2j + H (k_scale from K block j)
-      auto xh = [&](auto part, int i, int j, const BlockDma& bd) {
+      // softmax half-step of sub-tile i = 2j + H (k_scale from K block j);
+      // group 0 also issues its share of the block's DMA.  CHK: the sub-tile
+      // may be missing or be the wave's last (masked).
+      auto xh = [&](auto grpc, auto chk, auto part, int i, int j, const BlockDma& bd) {
         constexpr int H = decltype(part)::value;
-        constexpr int O0 = H == 0 ? 0 : OPH;
-        constexpr int O1 = H == 0 ? OPH : C::N_OPS;
-        if (i < n_sub) {
-          const float* ks =
-              reinterpret_cast<const float*>(smem + (j % C::NKS) * C::KSLOT + C::KS_OFF) + 32 * H;
-          xphase<O0, O1>(w, ks, hf, cq, i == n_sub - 1, lim - 32 * i - 4 * hf, bd, dl, junk, wave);
-        } else {
+        constexpr bool DMA = decltype(grpc)::value == 0;
+        constexpr int O0 = !DMA ? 0 : H == 0 ? 0 : OPH;
+        constexpr int O1 = !DMA ? 0 : H == 0 ? OPH : C::N_OPS;
+        constexpr bool CHK = decltype(chk)::value;
+        const float* ks =
+            reinterpret_cast<const float*>(smem + (j % C::NKS) * C::KSLOT + C::KS_OFF) + 32 * H;
+        if (!CHK || i < n_sub)
+          xphase<O0, O1, CHK>(w, ks, hf, cq, i == n_sub - 1, lim - 32 * i - 4 * hf, bd, dl, junk,
+                              wave);
+        else
           dma_ops<O0, O1>(bd, dl, junk, wave);
-        }
       };
       // product half-step of sub-tile i: V of block j (half VH), K of block
       // jk (half KH)
-      auto gh = [&](auto kh, auto vh_, int i, int j, int jk) {
-        if (i >= 0 && i < n_sub) {
+      auto gh = [&](auto chk, auto kh, auto vh_, int i, int j, int jk) {
+        if (!decltype(chk)::value || i < n_sub) {
           const uint32_t ks = sbase + (uint32_t)(jk % C::NKS) * C::KSLOT;
           const uint32_t vs = sbase + C::V_BASE + (uint32_t)(j & (C::NVS - 1)) * C::VSLOT;
           uint32_t vb[C::DV_TILES];
@@ -719,20 +729,37 @@ struct MfmaKernel {
       };
       using P0 = std::integral_constant<int, 0>;
       using P1 = std::integral_constant<int, 1>;
+      using Y = std::true_type;
+      using N = std::false_type;
       auto publish_block = [&]() {
         if constexpr (C::KLEAD == 3)
           publish<C::N_OPS>();  // batch j may stay in flight
         else
           publish<C::V_DMA>();  // batch j's K part must be in too
       };
-      for (int j = 0; j < nblocks; ++j) {
-        const BlockDma bd = blk(j);
-        xh(P0{}, 2 * j, j, bd);
-        gh(P1{}, P0{}, 2 * j, j, j);
-        xh(P1{}, 2 * j + 1, j, bd);
-        if (grp == 1) publish_block();
-        gh(P0{}, P1{}, 2 * j + 1, j, j + 1);
-        if (grp == 0) publish_block();
+      // One block of a group: X_{2j} G_{2j} X_{2j+1} G_{2j+1}, the barrier
+      // after it (group 0) or before its last product half-step (group 1).
+      auto block = [&](auto grpc, auto chk, int j) {
+        constexpr int GRP = decltype(grpc)::value;
+        BlockDma bd;
+        if constexpr (GRP == 0) bd = blk(j);
+        xh(grpc, chk, P0{}, 2 * j, j, bd);
+        gh(chk, P1{}, P0{}, 2 * j, j, j);
+        xh(grpc, chk, P1{}, 2 * j + 1, j, bd);
+        if constexpr (GRP == 1) publish_block();
+        gh(chk, P0{}, P1{}, 2 * j + 1, j, j + 1);
+        if constexpr (GRP == 0) publish_block();
+      };
+      // blocks whose four half-steps all exist and need no mask, then the rest
+      const int n_steady = min(nblocks, n_sub > 0 ? (n_sub - 1) / 2 : 0);
+      if (grp == 0) {
+        int j = 0;
+        for (; j < n_steady; ++j) block(P0{}, N{}, j);
+        for (; j < nblocks; ++j) block(P0{}, Y{}, j);
+      } else {
+        int j = 0;
+        for (; j < n_steady; ++j) block(P1{}, N{}, j);
+        for (; j < nblocks; ++j) block(P1{}, Y{}, j);
       }
       // the last batches requested nothing; drain, and let group 1 finish
       // its last products, before the rings are reused for the output
