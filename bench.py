@@ -22,6 +22,12 @@ cpu_baseline  the float64 CPU oracle on a bounded sample of the same
            workload: whole (sequence, head) pairs, as many as fit in about
            10 s, rated with the same metric FLOPs.
 
+    python bench.py --op quantize [--steps K] [--warmup W]
+times the per-row fp8 quantiser (mha_quantize_fp8) on the fp8 workload's Q
+(32768 tokens x 32 heads x 128, bf16) and prints its own JSON line: GB/s of
+algorithmic HBM bytes (input read + codes and scales written) against the
+8 TB/s HBM peak, with the CPU oracle quantiser timed on sampled rows.
+
     python bench.py --summarize-profile DIR --workload NAME
 writes profiles/<kernel>_<workload>.md from the rocprofv3 output under DIR
 (trace/, pmcA/, pmcB/, pmcC/ = FETCH_SIZE, pmcD/ = WRITE_SIZE, copy_fetch/,
@@ -58,15 +64,20 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 COPY_PROBE_MIB = 1024
 
 
+# the sources that decide what the attention kernel and its scheduler do on
+# the device (the other entry points of the library do not)
+KERNEL_SOURCES = ("attn_bf16.hip", "attn_fp8.hip", "attn_mfma.h", "common.h", "sched.hip")
+
+
 def kernel_sources_sha256() -> str:
-    """Hash of the library sources: a traffic figure is valid for these only."""
+    """Hash of the attention kernel's sources: a traffic figure is valid for
+    these only."""
     h = hashlib.sha256()
     src = os.path.join(ROOT, "head_attention_forward_fa_amd", "csrc")
-    for f in sorted(os.listdir(src)):
-        if f.endswith((".h", ".hip", ".cpp")):
-            h.update(f.encode())
-            with open(os.path.join(src, f), "rb") as fh:
-                h.update(fh.read())
+    for f in KERNEL_SOURCES:
+        h.update(f.encode())
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
@@ -309,12 +320,85 @@ def algorithmic_bytes(inp) -> float:
     return float(b)
 
 
+QUANT_WORKLOAD = "fp8_quant_bf16_t32768_h32_d128"
+HBM_PEAK_GBS = 8000.0
+
+
+def bench_quantize(a, lib, dev) -> int:
+    """Per-row fp8 quantiser on the fp8 workload's Q tensor (bf16 rows)."""
+    import torch
+    from head_attention_forward_fa_amd import _native, mha_quantize_fp8
+
+    T, H, D = 32768, 32, 128
+    x_np = mi.make_rows((T, H, D), dtype="bf16", seed=11, magnitude_sigma=0.5)
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    codes = torch.empty((T, H, D), dtype=torch.uint8, device=dev)
+    scales = torch.empty((T, H), dtype=torch.float32, device=dev)
+    rows = T * H
+    nbytes = rows * D * 2 + rows * D + rows * 4  # read x, write codes and scales
+    for _ in range(a.warmup):
+        mha_quantize_fp8(x, codes=codes, scales=scales)
+    torch.cuda.synchronize()
+    # kernel-only durations: the library records these HIP events right
+    # before and after its launch (mha_fwd_set_kernel_events)
+    hip = HipEvents()
+    kev = [(hip.create(), hip.create()) for _ in range(a.steps)]
+    for e0, e1 in kev:
+        _native.check(lib.mha_fwd_set_kernel_events(e0, e1))
+        mha_quantize_fp8(x, codes=codes, scales=scales)
+    _native.check(lib.mha_fwd_set_kernel_events(None, None))
+    torch.cuda.synchronize()
+    ms = [hip.elapsed_ms(e0, e1) for e0, e1 in kev]
+    for e0, e1 in kev:
+        hip.destroy(e0)
+        hip.destroy(e1)
+    mean_ms = float(np.mean(ms))
+    gbs = nbytes / (mean_ms * 1e-3) / 1e9
+    print(f"[bench] quantise {rows} rows x {D}: {mean_ms * 1e3:.1f} us (min {min(ms) * 1e3:.1f}), "
+          f"{gbs:.0f} GB/s, {100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f}",
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not a.no_cpu_baseline:
+        from oracle import quantize as oq
+        flat = x_np.reshape(rows, D)
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(a.cpu_budget, 10.0) and done < rows:
+            oq.quantize_bf16_rows(flat[done:done + 65536])
+            done += min(65536, rows - done)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(done * (D * 3 + 4) / dt / 1e9, 4), "unit": "GB/s",
+               "cores": 1, "kind": "oracle",
+               "sample": f"first {done} of {rows} rows (numpy, one thread)"}
+    line = {
+        "metric": "fp8 per-row quantisation GB/s (bf16 read + codes and scales written)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(mean_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 -> fp8-e4m3",
+        "data": "synthetic",
+        "config": {"workload": QUANT_WORKLOAD, "rows": rows, "cols": D,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=mi.WORKLOAD_ORDER)
+    ap.add_argument("--op", default="attention", choices=("attention", "quantize"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -348,6 +432,8 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(f"[bench] copied {a.copy_probe_mib} MiB five times", file=sys.stderr)
         return 0
+    if a.op == "quantize":
+        return bench_quantize(a, lib, dev)
     inp = mi.workload(a.workload)
     print(f"[bench] workload {inp.name}: T={inp.total_tokens} Hq={inp.num_heads} "
           f"Hkv={inp.num_kv_heads} D={inp.head_dim_nope}+{inp.head_dim_rope}/{inp.v_dim}",

@@ -22,7 +22,7 @@ MHA_ERR_UNSUPPORTED = 2
 MHA_ERR_HIP = 3
 
 EXPORTS = ("mha_fwd", "mha_fwd_last_error", "mha_fwd_supported", "mha_fwd_kernel_info",
-           "mha_fwd_set_kernel_events", "mha_sched_visit")
+           "mha_fwd_set_kernel_events", "mha_sched_visit", "mha_quantize_fp8")
 
 _lib = None
 
@@ -63,6 +63,8 @@ def load() -> ctypes.CDLL:
     lib.mha_fwd_set_kernel_events.restype = ctypes.c_int
     lib.mha_sched_visit.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.mha_sched_visit.restype = ctypes.c_int
+    lib.mha_quantize_fp8.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp]
+    lib.mha_quantize_fp8.restype = ctypes.c_int
     _lib = lib
     return lib
 

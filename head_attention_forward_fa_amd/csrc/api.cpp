@@ -297,4 +297,29 @@ int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen
   return MHA_OK;
 }
 
+int mha_quantize_fp8(const void* x, int32_t x_dtype, int64_t rows, int32_t cols,
+                     uint8_t* codes, float* scales, void* stream) {
+  g_err.clear();
+  if (x_dtype != MHA_DTYPE_F32 && x_dtype != MHA_DTYPE_BF16)
+    return fail(MHA_ERR_INVALID_ARG, "x_dtype must be MHA_DTYPE_F32 or MHA_DTYPE_BF16");
+  if (rows < 0 || rows > INT_MAX) return fail(MHA_ERR_INVALID_ARG, "rows must be in [0, 2^31)");
+  if (cols < 8 || cols > 512 || cols % 8 != 0)
+    return fail(MHA_ERR_INVALID_ARG, "cols must be a multiple of 8 in [8, 512]");
+  if (rows == 0) return MHA_OK;
+  if (!x || !codes || !scales)
+    return fail(MHA_ERR_INVALID_ARG, "x, codes, scales must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(x) % 16 != 0 || reinterpret_cast<uintptr_t>(codes) % 8 != 0 ||
+      reinterpret_cast<uintptr_t>(scales) % 4 != 0)
+    return fail(MHA_ERR_INVALID_ARG, "x must be 16-byte, codes 8-byte, scales 4-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (g_ev_start && (e = hipEventRecord(g_ev_start, s)) != hipSuccess)
+    return fail_hip(e, "hipEventRecord");
+  e = mha::launch_fp8_quant(x, x_dtype == MHA_DTYPE_BF16, rows, cols, codes, scales, s);
+  if (e != hipSuccess) return fail_hip(e, "quantiser launch");
+  if (g_ev_stop && (e = hipEventRecord(g_ev_stop, s)) != hipSuccess)
+    return fail_hip(e, "hipEventRecord");
+  return MHA_OK;
+}
+
 }  // extern "C"

@@ -23,6 +23,11 @@ hipError_t launch_sched_visit(int batch, int num_heads, int tiles, const i32x4* 
                               SchedState* st, int* visits, int grid,
                               hipStream_t stream);
 
+// Per-row fp8 quantisation (quant.hip): rows x cols input (bf16 bits or
+// float32), cols % 8 == 0, 8 <= cols <= 512.
+hipError_t launch_fp8_quant(const void* x, bool bf16, int64_t rows, int cols, uint8_t* codes,
+                            float* scales, hipStream_t stream);
+
 // A kernel variant: its launcher and its occupancy (resident workgroups per
 // CU at its LDS and register footprint, computed once per device).
 struct Variant {

@@ -1,0 +1,126 @@
+// Per-token fp8 quantisation of Q / K rows: one float32 scale per row of D
+// elements and the row's OCP E4M3 codes.  This is the step in front of the
+// fp8 attention path, whose Q and K come as 8-bit codes with a per-token
+// scale (SM100AttentionSMem, Parameters: scale_dtype_; Methods q_scale_smem /
+// k_scale_smem).  Reading of how the codes are made (the pages leave it
+// open):
+//
+//   scale = amax(|row|) / 448        (448 = largest finite E4M3; scale 1 for a
+//                                     row of zeros)
+//   code  = round-to-nearest-even E4M3 of clamp(x / scale, -448, 448)
+//
+// with IEEE float32 division, so the codes are exact functions of the input.
+//
+// HBM-bound: each row is read once (D bf16 or float32 elements) and written
+// once (D codes + 4 bytes of scale).  A row is spread over LPR lanes (8
+// consecutive elements per lane, one 16- or 32-byte load), its amax is a
+// butterfly over those lanes, and each lane writes its 8 codes as one
+// 8-byte store, so a wave moves 64 x 16 (bf16) contiguous bytes per load
+// instruction.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace mha {
+
+namespace {
+
+constexpr float kE4M3Max = 448.0f;
+constexpr int kQuantThreads = 256;
+
+// Two float32 values already inside [-448, 448] -> two E4M3 codes in the low
+// 16 bits (first value in the low byte): v_cvt_pk_fp8_f32, round to nearest
+// even, OCP E4M3 on gfx950.
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* x, size_t elem, float (&v)[8]) {
+  if constexpr (BF16) {
+    const i32x4 w = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(x) + elem);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __builtin_bit_cast(float, (uint32_t)w[i] << 16);
+      v[2 * i + 1] = __builtin_bit_cast(float, (uint32_t)w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + elem);
+    const f32x4 a = p[0], b = p[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
+  }
+}
+
+// LPR lanes per row (a power of two, LPR * 8 >= cols); 256 / LPR rows per
+// workgroup.
+template <bool BF16, int LPR>
+__global__ __launch_bounds__(kQuantThreads) void fp8_quant_rows_kernel(const void* __restrict__ x,
+                                                                      int64_t rows, int cols,
+                                                                      uint8_t* __restrict__ codes,
+                                                                      float* __restrict__ scales) {
+  constexpr int RPB = kQuantThreads / LPR;
+  const int c = threadIdx.x % LPR;  // 8-element chunk of the row
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const bool live = row < rows && c * 8 < cols;
+  float v[8];
+  float amax = 0.f;
+  if (live) {
+    load8<BF16>(x, (size_t)row * cols + c * 8, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
+  // butterfly over the row's lanes (aligned groups of LPR lanes)
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+  const float scale = amax > 0.f ? amax / kE4M3Max : 1.0f;
+  if (!live) return;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const float a = fminf(fmaxf(v[i] / scale, -kE4M3Max), kE4M3Max);
+    const float b = fminf(fmaxf(v[i + 1] / scale, -kE4M3Max), kE4M3Max);
+    const uint32_t p = cvt2(a, b);
+    if (i < 4)
+      lo |= p << (8 * i);
+    else
+      hi |= p << (8 * (i - 4));
+  }
+  *reinterpret_cast<i32x2*>(codes + (size_t)row * cols + c * 8) = i32x2{(int)lo, (int)hi};
+  if (c == 0) scales[row] = scale;
+}
+
+template <bool BF16, int LPR>
+hipError_t launch_lpr(const void* x, int64_t rows, int cols, uint8_t* codes, float* scales,
+                      hipStream_t stream) {
+  constexpr int RPB = kQuantThreads / LPR;
+  const int64_t blocks = (rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL((fp8_quant_rows_kernel<BF16, LPR>), dim3((unsigned)blocks),
+                     dim3(kQuantThreads), 0, stream, x, rows, cols, codes, scales);
+  return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_dtype(const void* x, int64_t rows, int cols, uint8_t* codes, float* scales,
+                        hipStream_t stream) {
+  const int chunks = cols / 8;
+  if (chunks <= 8) return launch_lpr<BF16, 8>(x, rows, cols, codes, scales, stream);
+  if (chunks <= 16) return launch_lpr<BF16, 16>(x, rows, cols, codes, scales, stream);
+  if (chunks <= 32) return launch_lpr<BF16, 32>(x, rows, cols, codes, scales, stream);
+  return launch_lpr<BF16, 64>(x, rows, cols, codes, scales, stream);
+}
+
+}  // namespace
+
+hipError_t launch_fp8_quant(const void* x, bool bf16, int64_t rows, int cols, uint8_t* codes,
+                            float* scales, hipStream_t stream) {
+  return bf16 ? launch_dtype<true>(x, rows, cols, codes, scales, stream)
+              : launch_dtype<false>(x, rows, cols, codes, scales, stream);
+}
+
+}  // namespace mha

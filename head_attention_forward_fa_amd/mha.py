@@ -143,3 +143,35 @@ def mha_sched_visit(cu_seqlens: torch.Tensor, max_seqlen: int, num_heads: int,
                                         int(block_m), int(grid), _ptr(visits), stream)
     nat.check(st)
     return visits
+
+
+def mha_quantize_fp8(x: torch.Tensor, *, codes: Optional[torch.Tensor] = None,
+                     scales: Optional[torch.Tensor] = None):
+    """Per-row fp8 quantisation on the GPU (mha_quantize_fp8 of the C ABI).
+
+    x: [..., D] float32 or bfloat16, contiguous, on a GPU.  Returns (codes,
+    scales): codes uint8 [..., D] (OCP E4M3 bit patterns; view them as
+    torch.float8_e4m3fn if wanted), scales float32 [...], one per row of D
+    elements; a [T, H, D] Q or K gives the q / k and q_scale / k_scale
+    arguments of mha_fwd's FP8_E4M3 path.
+    """
+    if x.device.type != "cuda":
+        raise ValueError("x must be on a GPU device")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x must be float32 or bfloat16")
+    if x.dim() < 1 or not x.is_contiguous():
+        raise ValueError("x must be contiguous with at least one dimension")
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    c = codes if codes is not None else torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    s = scales if scales is not None else torch.empty(x.shape[:-1], dtype=torch.float32,
+                                                      device=x.device)
+    _need(c, "codes", x.device, torch.uint8, tuple(x.shape))
+    _need(s, "scales", x.device, torch.float32, tuple(x.shape[:-1]))
+    code = nat.MHA_DTYPE_BF16 if x.dtype == torch.bfloat16 else nat.MHA_DTYPE_F32
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        st = nat.load().mha_quantize_fp8(_ptr(x), code, int(rows), int(D), _ptr(c), _ptr(s),
+                                         stream)
+    nat.check(st)
+    return c, s

@@ -147,7 +147,8 @@ int mha_fwd_kernel_info(int32_t dtype, int32_t head_dim_nope, int32_t head_dim_r
  * caller, who keeps ownership) that every following mha_fwd call made by the
  * same host thread records on its stream immediately before and after the
  * attention kernel, so that the kernel's own duration can be read without a
- * profiler (the scheduler prepass that precedes it is outside the pair).
+ * profiler (the scheduler prepass that precedes it is outside the pair);
+ * mha_quantize_fp8 records the same pair around its kernel.
  * NULL, NULL switches the hook off; exactly one NULL is MHA_ERR_INVALID_ARG.
  * A call whose outputs are empty (max_seqlen == 0) records nothing.
  */
@@ -155,8 +156,9 @@ int mha_fwd_set_kernel_events(void* start_event, void* stop_event);
 
 /*
  * mha_sched_visit -- diagnostic for the persistent tile scheduler
- * (MHATileScheduler: "maps work tiles to thread blocks, advances the per-CTA
- * state through the work grid").  Builds the work table exactly as mha_fwd
+ * (MHATileScheduler, class description: the scheduler hands out work tiles
+ * to workgroups and moves each one on to its next tile).  Builds the work
+ * table exactly as mha_fwd
  * does for (cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads, causal,
  * block_m) and runs `grid` workgroups (0 = the size mha_fwd would use for
  * this block_m) that only fetch work items and add 1 to
@@ -169,6 +171,36 @@ int mha_fwd_set_kernel_events(void* start_event, void* stop_event);
 int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
                     int32_t num_heads, int32_t num_kv_heads, int32_t causal,
                     int32_t block_m, int32_t grid, int32_t* visits, void* stream);
+
+/*
+ * mha_quantize_fp8 -- per-token fp8 quantisation of Q or K rows, the step in
+ * front of the FP8_E4M3 path (whose Q and K are E4M3 codes with one float32
+ * scale per token and head: SM100AttentionSMem, Parameters: scale_dtype_;
+ * Methods q_scale_smem / k_scale_smem).  The pages do not say how the codes
+ * are made; this library's reading, per row r of `cols` elements:
+ *
+ *     scales[r]   = amax_c |x[r, c]| / 448      (1 for a row of zeros)
+ *     codes[r, c] = E4M3 code nearest to clamp(x[r, c] / scales[r], -448, 448),
+ *                   ties to the even code
+ *
+ * with IEEE float32 division, so codes and scales are exact functions of x.
+ * A [T, H, D] tensor is rows = T * H, cols = D; the results feed mha_fwd as
+ * q / k and q_scale / k_scale directly.
+ *
+ *   x       device, rows x cols, contiguous; float32 (x_dtype MHA_DTYPE_F32)
+ *           or bfloat16 (MHA_DTYPE_BF16); 16-byte aligned; finite values
+ *           (NaN / Inf inputs give unspecified codes)
+ *   codes   device uint8, rows x cols, written; 8-byte aligned
+ *   scales  device float32, rows, written
+ *   rows    >= 0 (0: nothing is launched), < 2^31
+ *   cols    multiple of 8, 8 .. 512
+ * MHA_ERR_INVALID_ARG for a NULL pointer (rows > 0), a misaligned pointer, an
+ * unknown x_dtype or a size outside these ranges; MHA_ERR_HIP if the launch
+ * fails.  HBM-bound: reads rows * cols * sizeof(x), writes rows * (cols + 4)
+ * bytes.
+ */
+int mha_quantize_fp8(const void* x, int32_t x_dtype, int64_t rows, int32_t cols,
+                     uint8_t* codes, float* scales, void* stream);
 
 #ifdef __cplusplus
 }

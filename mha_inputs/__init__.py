@@ -190,3 +190,17 @@ def attention_flops(inp: Inputs) -> float:
     lens = inp.seqlens.astype(np.float64)
     f = 4.0 * inp.num_heads * float(np.sum(lens * lens)) * d
     return f / 2.0 if inp.causal else f
+
+
+def make_rows(shape, *, dtype: str = "bf16", seed: int = 0,
+              magnitude_sigma: float = 1.0) -> np.ndarray:
+    """Rows [..., D]: N(0,1) elements times one lognormal(0, sigma) magnitude
+    per row, as float32 values (dtype "f32") or bfloat16 bit patterns
+    ("bf16").  Inputs of the per-row fp8 quantiser."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(dtype)
+    rng = np.random.default_rng(seed)
+    x = _normal(rng, tuple(shape))
+    mag = rng.lognormal(0.0, magnitude_sigma, size=tuple(shape[:-1]) + (1,)).astype(np.float32)
+    x = (x * mag).astype(np.float32)
+    return x if dtype == "f32" else to_bf16_bits(x)

@@ -94,7 +94,7 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
 def dequantize_per_token(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """fp8 codes [T, H, D] and scales [T, H] -> float64 values code * scale.
 
-    One scale per (token, head) row ("per-token scale used for Q and K",
+    One scale per (token, head) row (Q and K carry one scale per token:
     SM100AttentionSMem, Parameters: scale_dtype_; q_scale_smem holds BM of
     them per Q tile, k_scale_smem BN per K buffer).  The product of an E4M3
     value and a float32 scale is exact in float64.

@@ -118,3 +118,27 @@ def test_python_binding_rejects_cpu_tensors():
     q = torch.zeros(2, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         mha_fwd(q, q, q, cu_seqlens=torch.tensor([0, 2], dtype=torch.int32), max_seqlen=2)
+
+
+QBAD = [
+    dict(dtype=nat.MHA_DTYPE_FP8_E4M3), dict(dtype=9),
+    dict(rows=-1), dict(rows=1 << 31), dict(cols=0), dict(cols=4), dict(cols=12),
+    dict(cols=520), dict(x=None), dict(codes=None), dict(scales=None),
+    dict(x=FAKE + 8), dict(codes=FAKE + 4), dict(scales=FAKE + 2),
+]
+
+
+@pytest.mark.parametrize("over", QBAD)
+def test_quantize_fp8_validation(over):
+    a = dict(x=FAKE, dtype=nat.MHA_DTYPE_BF16, rows=16, cols=128, codes=FAKE, scales=FAKE)
+    a.update(over)
+    lib = nat.load()
+    st = lib.mha_quantize_fp8(a["x"], a["dtype"], a["rows"], a["cols"], a["codes"], a["scales"],
+                              None)
+    assert st == nat.MHA_ERR_INVALID_ARG
+    assert lib.mha_fwd_last_error()
+
+
+def test_quantize_fp8_zero_rows_is_a_no_op():
+    lib = nat.load()
+    assert lib.mha_quantize_fp8(None, nat.MHA_DTYPE_F32, 0, 64, None, None, None) == nat.MHA_OK
