@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline]
 
-A step is one mha_fwd call (scheduler prepass + attention kernel) over the
-whole workload, inputs resident in HBM.  Default workload: bf16 causal
+A step is one mha_fwd call (scheduler prepass + attention kernel; with
+--splits N > 1 also the split merge) over the whole workload, inputs
+resident in HBM.  Default workload: bf16 causal
 prefill, B=4, H=32, S=4096, D=128.  Prints one JSON line.
 
 value      attention TFLOP/s = metric FLOPs (4*B*H*S^2*D, halved for causal)
@@ -397,7 +398,11 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=mi.WORKLOAD_ORDER)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=mi.WORKLOAD_ORDER + list(mi.EXTRA_WORKLOADS))
+    ap.add_argument("--splits", type=int, default=1,
+                    help="split-KV: cut every query tile's keys into this many work items "
+                         "(mha_fwd_splitkv) and merge")
     ap.add_argument("--op", default="attention", choices=("attention", "quantize"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -457,11 +462,18 @@ def main(argv=None):
     o = torch.empty((inp.total_tokens, inp.num_heads, inp.v_dim),
                     dtype=torch.float32 if inp.dtype == "f32" else torch.bfloat16, device=dev)
     lse = torch.empty((inp.num_heads, inp.total_tokens), dtype=torch.float32, device=dev)
+    part = {}
+    if a.splits > 1:
+        part = dict(num_splits=a.splits,
+                    o_partial=torch.empty((a.splits, inp.total_tokens, inp.num_heads, inp.v_dim),
+                                          dtype=torch.float32, device=dev),
+                    lse_partial=torch.empty((a.splits, inp.num_heads, inp.total_tokens),
+                                            dtype=torch.float32, device=dev))
 
     def step():
         mha_fwd(q, k, v, causal=inp.causal, cu_seqlens=cu, max_seqlen=inp.max_seqlen,
                 q_rope=qr, k_rope=kr, q_scale=qs, k_scale=ks,
-                softmax_scale=inp.softmax_scale, out=o, lse=lse)
+                softmax_scale=inp.softmax_scale, out=o, lse=lse, **part)
 
     for _ in range(a.warmup):
         step()
@@ -529,6 +541,7 @@ def main(argv=None):
             "head_dim_rope": inp.head_dim_rope,
             "v_dim": inp.v_dim,
             "causal": inp.causal,
+            "num_splits": a.splits,
             "parallelism": "single-gpu",
         },
         "roofline": {

@@ -22,7 +22,8 @@ MHA_ERR_UNSUPPORTED = 2
 MHA_ERR_HIP = 3
 
 EXPORTS = ("mha_fwd", "mha_fwd_last_error", "mha_fwd_supported", "mha_fwd_kernel_info",
-           "mha_fwd_set_kernel_events", "mha_sched_visit", "mha_quantize_fp8")
+           "mha_fwd_set_kernel_events", "mha_sched_visit", "mha_quantize_fp8",
+           "mha_fwd_splitkv", "mha_combine_splits")
 
 _lib = None
 
@@ -65,6 +66,17 @@ def load() -> ctypes.CDLL:
     lib.mha_sched_visit.restype = ctypes.c_int
     lib.mha_quantize_fp8.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp]
     lib.mha_quantize_fp8.restype = ctypes.c_int
+    lib.mha_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp,       # q k v o lse
+                                    vp, i32, i32,             # cu_seqlens batch max_seqlen
+                                    i32, i32,                 # num_heads num_kv_heads
+                                    i32, i32, i32,            # Dn Dr Dv
+                                    vp, vp,                   # q_rope k_rope
+                                    i32, f32, i32,            # causal softmax_scale dtype
+                                    vp, vp,                   # q_scale k_scale
+                                    i32, i32, vp, vp, vp]     # T num_splits o_part lse_part stream
+    lib.mha_fwd_splitkv.restype = ctypes.c_int
+    lib.mha_combine_splits.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.mha_combine_splits.restype = ctypes.c_int
     _lib = lib
     return lib
 

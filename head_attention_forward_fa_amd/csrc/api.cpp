@@ -106,9 +106,9 @@ struct Plan {
 };
 
 int make_plan(int batch, int max_seqlen, int num_heads, int num_kv_heads, int block_m,
-              Plan* plan) {
+              int num_splits, Plan* plan) {
   long long tiles = ((long long)max_seqlen + block_m - 1) / block_m;
-  long long cap = (long long)num_heads * batch * tiles;
+  long long cap = (long long)num_heads * batch * tiles * num_splits;
   if (tiles >= mha::kMaxQTilesPerSeq || cap > INT_MAX / 2)
     return fail(MHA_ERR_INVALID_ARG, "problem too large for the work table");
   long long groups = (long long)batch * num_kv_heads;
@@ -122,7 +122,8 @@ int make_plan(int batch, int max_seqlen, int num_heads, int num_kv_heads, int bl
 
 int check_scalars(int32_t batch, int32_t max_seqlen, int32_t num_heads,
                   int32_t num_kv_heads) {
-  if (batch < 1) return fail(MHA_ERR_INVALID_ARG, "batch must be >= 1");
+  if (batch < 1 || batch >= mha::kMaxBatch)
+    return fail(MHA_ERR_INVALID_ARG, "batch must be in [1, 2^24)");
   if (max_seqlen < 0) return fail(MHA_ERR_INVALID_ARG, "max_seqlen must be >= 0");
   if (num_heads < 1 || num_kv_heads < 1)
     return fail(MHA_ERR_INVALID_ARG, "num_heads and num_kv_heads must be >= 1");
@@ -143,12 +144,18 @@ int mha_fwd_supported(int32_t dtype, int32_t head_dim_nope, int32_t head_dim_rop
   return mha::find_variant(dtype, head_dim_nope, head_dim_rope, v_dim) != nullptr;
 }
 
-int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-            const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen, int32_t num_heads,
-            int32_t num_kv_heads, int32_t head_dim_nope, int32_t head_dim_rope, int32_t v_dim,
-            const void* q_rope, const void* k_rope, int32_t causal, float softmax_scale,
-            int32_t dtype, const float* q_scale, const float* k_scale, void* stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// mha_fwd, and the first half of mha_fwd_splitkv (num_splits > 1: partial
+// results to o_part / lse_part, which the caller has checked).
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+             const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen, int32_t num_heads,
+             int32_t num_kv_heads, int32_t head_dim_nope, int32_t head_dim_rope, int32_t v_dim,
+             const void* q_rope, const void* k_rope, int32_t causal, float softmax_scale,
+             int32_t dtype, const float* q_scale, const float* k_scale, int32_t total_tokens,
+             int32_t num_splits, float* o_part, float* lse_part, void* stream) {
   int rc = check_scalars(batch, max_seqlen, num_heads, num_kv_heads);
   if (rc) return rc;
   if (head_dim_nope < 1 || head_dim_rope < 0 || v_dim < 1)
@@ -165,6 +172,8 @@ int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   if (max_seqlen == 0) return MHA_OK;
   if (!q || !k || !v || !o || !lse || !cu_seqlens)
     return fail(MHA_ERR_INVALID_ARG, "q, k, v, o, lse, cu_seqlens must be non-NULL");
+  if (num_splits > 1 && !var->launch_split)
+    return fail(MHA_ERR_UNSUPPORTED, "split-KV runs on the bf16 / fp8 kernels only");
   if ((q_rope == nullptr) != (k_rope == nullptr))
     return fail(MHA_ERR_INVALID_ARG, "q_rope and k_rope must both be given or both NULL");
   if ((head_dim_rope > 0) != (q_rope != nullptr))
@@ -174,7 +183,7 @@ int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     return fail(MHA_ERR_INVALID_ARG, "q_scale and k_scale must be given iff dtype is FP8_E4M3");
 
   Plan plan;
-  rc = make_plan(batch, max_seqlen, num_heads, num_kv_heads, var->block_m, &plan);
+  rc = make_plan(batch, max_seqlen, num_heads, num_kv_heads, var->block_m, num_splits, &plan);
   if (rc) return rc;
 
   const float sigma =
@@ -191,7 +200,7 @@ int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   auto* scratch = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
 
   e = mha::launch_prepass(cu_seqlens, batch, num_heads, num_kv_heads, causal, var->block_m,
-                          var->block_n, plan.capacity, table, st, scratch, s);
+                          var->block_n, num_splits, plan.capacity, table, st, scratch, s);
   if (e != hipSuccess) return fail_hip(e, "scheduler prepass launch");
 
   mha::AttnParams p;
@@ -213,6 +222,10 @@ int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   p.group = num_heads / num_kv_heads;
   p.causal = causal;
   p.scale_log2 = sigma * 1.4426950408889634f;
+  p.num_splits = num_splits;
+  p.part_tokens = total_tokens;
+  p.o_part = num_splits > 1 ? o_part : nullptr;
+  p.lse_part = num_splits > 1 ? lse_part : nullptr;
 
   long long grid = (long long)cu_count(dev) * var->blocks_per_cu();
   if (grid > plan.capacity) grid = plan.capacity;
@@ -221,12 +234,80 @@ int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
     e = hipEventRecord(g_ev_start, s);
     if (e != hipSuccess) return fail_hip(e, "hipEventRecord (start)");
   }
-  e = var->launch(p, (int)grid, s);
+  e = (num_splits > 1 ? var->launch_split : var->launch)(p, (int)grid, s);
   if (e != hipSuccess) return fail_hip(e, "attention kernel launch");
   if (g_ev_stop) {
     e = hipEventRecord(g_ev_stop, s);
     if (e != hipSuccess) return fail_hip(e, "hipEventRecord (stop)");
   }
+  if (num_splits > 1) {
+    e = mha::launch_combine(o_part, lse_part, num_splits, total_tokens, num_heads, v_dim,
+                            dtype != MHA_DTYPE_F32, o, lse, s);
+    if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
+  }
+  return MHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+            const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen, int32_t num_heads,
+            int32_t num_kv_heads, int32_t head_dim_nope, int32_t head_dim_rope, int32_t v_dim,
+            const void* q_rope, const void* k_rope, int32_t causal, float softmax_scale,
+            int32_t dtype, const float* q_scale, const float* k_scale, void* stream) {
+  g_err.clear();
+  return fwd_impl(q, k, v, o, lse, cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads,
+                  head_dim_nope, head_dim_rope, v_dim, q_rope, k_rope, causal, softmax_scale,
+                  dtype, q_scale, k_scale, 0, 1, nullptr, nullptr, stream);
+}
+
+int mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim_nope,
+                    int32_t head_dim_rope, int32_t v_dim, const void* q_rope, const void* k_rope,
+                    int32_t causal, float softmax_scale, int32_t dtype, const float* q_scale,
+                    const float* k_scale, int32_t total_tokens, int32_t num_splits,
+                    float* o_partial, float* lse_partial, void* stream) {
+  g_err.clear();
+  if (num_splits < 1 || num_splits > mha::kMaxSplits)
+    return fail(MHA_ERR_INVALID_ARG, "num_splits must be in [1, 64]");
+  if (total_tokens < 0) return fail(MHA_ERR_INVALID_ARG, "total_tokens must be >= 0");
+  if (dtype == MHA_DTYPE_F32)
+    return fail(MHA_ERR_UNSUPPORTED, "split-KV runs on the bf16 / fp8 kernels only");
+  if (num_splits > 1 && max_seqlen > 0 && (!o_partial || !lse_partial))
+    return fail(MHA_ERR_INVALID_ARG, "o_partial and lse_partial must be non-NULL");
+  if (num_splits > 1 && max_seqlen > 0 &&
+      (reinterpret_cast<uintptr_t>(o_partial) % 16 != 0 ||
+       reinterpret_cast<uintptr_t>(lse_partial) % 4 != 0))
+    return fail(MHA_ERR_INVALID_ARG, "o_partial must be 16-byte and lse_partial 4-byte aligned");
+  return fwd_impl(q, k, v, o, lse, cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads,
+                  head_dim_nope, head_dim_rope, v_dim, q_rope, k_rope, causal, softmax_scale,
+                  dtype, q_scale, k_scale, total_tokens, num_splits, o_partial, lse_partial,
+                  stream);
+}
+
+int mha_combine_splits(const float* o_partial, const float* lse_partial, int32_t num_splits,
+                       int32_t total_tokens, int32_t num_heads, int32_t v_dim, int32_t out_dtype,
+                       void* o, float* lse, void* stream) {
+  g_err.clear();
+  if (num_splits < 1 || num_splits > mha::kMaxSplits)
+    return fail(MHA_ERR_INVALID_ARG, "num_splits must be in [1, 64]");
+  if (total_tokens < 0 || num_heads < 1)
+    return fail(MHA_ERR_INVALID_ARG, "total_tokens must be >= 0 and num_heads >= 1");
+  if (v_dim != 64 && v_dim != 128) return fail(MHA_ERR_UNSUPPORTED, "v_dim must be 64 or 128");
+  if (out_dtype != MHA_DTYPE_F32 && out_dtype != MHA_DTYPE_BF16)
+    return fail(MHA_ERR_INVALID_ARG, "out_dtype must be MHA_DTYPE_F32 or MHA_DTYPE_BF16");
+  if (total_tokens == 0) return MHA_OK;
+  if (!o_partial || !lse_partial || !o || !lse)
+    return fail(MHA_ERR_INVALID_ARG, "o_partial, lse_partial, o, lse must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(o_partial) % 16 != 0 || reinterpret_cast<uintptr_t>(o) % 16 != 0)
+    return fail(MHA_ERR_INVALID_ARG, "o_partial and o must be 16-byte aligned");
+  hipError_t e = mha::launch_combine(o_partial, lse_partial, num_splits, total_tokens, num_heads,
+                                     v_dim, out_dtype == MHA_DTYPE_BF16, o, lse,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
   return MHA_OK;
 }
 
@@ -275,7 +356,7 @@ int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen
   if (grid < 0) return fail(MHA_ERR_INVALID_ARG, "grid must be >= 0");
   if (max_seqlen == 0) return MHA_OK;
   Plan plan;
-  rc = make_plan(batch, max_seqlen, num_heads, num_kv_heads, block_m, &plan);
+  rc = make_plan(batch, max_seqlen, num_heads, num_kv_heads, block_m, 1, &plan);
   if (rc) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   int dev = 0;
@@ -288,7 +369,7 @@ int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen
   auto* table = reinterpret_cast<mha::i32x4*>(ws + kStateBytes);
   auto* scratch = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
   e = mha::launch_prepass(cu_seqlens, batch, num_heads, num_kv_heads, causal, block_m, block_n,
-                          plan.capacity, table, st, scratch, s);
+                          1, plan.capacity, table, st, scratch, s);
   if (e != hipSuccess) return fail_hip(e, "scheduler prepass launch");
   if (grid == 0) grid = cu_count(dev) * 2;
   const int tiles = (int)(((long long)max_seqlen + block_m - 1) / block_m);

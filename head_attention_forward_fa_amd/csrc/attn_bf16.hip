@@ -7,9 +7,9 @@ using C64 = MfmaCfg<64, 0, 64, false>;
 using C128 = MfmaCfg<128, 0, 128, false>;
 using CRope = MfmaCfg<128, 64, 128, false>;
 const Variant kBf16[] = {
-    {launch_mfma<C64>, blocks_mfma<C64>, C64::BM, C64::BN, C64::LDS},
-    {launch_mfma<C128>, blocks_mfma<C128>, C128::BM, C128::BN, C128::LDS},
-    {launch_mfma<CRope>, blocks_mfma<CRope>, CRope::BM, CRope::BN, CRope::LDS},
+    {launch_mfma<C64>, blocks_mfma<C64>, C64::BM, C64::BN, C64::LDS, launch_mfma<C64, true>},
+    {launch_mfma<C128>, blocks_mfma<C128>, C128::BM, C128::BN, C128::LDS, launch_mfma<C128, true>},
+    {launch_mfma<CRope>, blocks_mfma<CRope>, CRope::BM, CRope::BN, CRope::LDS, launch_mfma<CRope, true>},
 };
 }  // namespace
 

@@ -6,7 +6,7 @@ namespace mha {
 namespace {
 using C128 = MfmaCfg<128, 0, 128, true>;
 const Variant kFp8[] = {
-    {launch_mfma<C128>, blocks_mfma<C128>, C128::BM, C128::BN, C128::LDS},
+    {launch_mfma<C128>, blocks_mfma<C128>, C128::BM, C128::BN, C128::LDS, launch_mfma<C128, true>},
 };
 }  // namespace
 

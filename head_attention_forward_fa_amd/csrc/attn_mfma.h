@@ -286,10 +286,11 @@ struct MfmaKernel {
     const char* v;
     uint32_t rows_stride;        // [T, Hkv] rows per block: BN * Hkv
     uint32_t span_full, span_last;  // [T, Hkv] rows a full / the last block spans
-    int nblocks;
+    int nblocks;                 // blocks of the tile's visible keys
+    int jlo, jhi;                // the blocks this item loads (its key split)
   };
   static __device__ __forceinline__ DmaSrc dma_src(const AttnParams& p, int s0, int L, int g,
-                                                  int nblocks) {
+                                                  int nblocks, int jlo, int jhi) {
     const uint32_t Hkv = (uint32_t)p.num_kv_heads;
     const size_t row0 = (size_t)s0 * Hkv + (uint32_t)g;
     DmaSrc d;
@@ -301,6 +302,8 @@ struct MfmaKernel {
     d.span_full = (C::BN - 1) * Hkv + 1;
     d.span_last = (uint32_t)(min(L - (nblocks - 1) * C::BN, C::BN) - 1) * Hkv + 1;
     d.nblocks = nblocks;
+    d.jlo = jlo;
+    d.jhi = jhi;
     return d;
   }
 
@@ -316,13 +319,20 @@ struct MfmaKernel {
                                                     uint32_t span) {
     return rsrc_of(base + (size_t)((uint32_t)blk * d.rows_stride) * RB, span * RB);
   }
+  template <bool SPLIT>
   static __device__ __forceinline__ BlockDma block_dma(const DmaSrc& d, uint32_t sbase, int wave,
                                                       int kblk, int vblk) {
-    const uint32_t kspan =
-        kblk < d.nblocks - 1 ? d.span_full : (kblk == d.nblocks - 1 ? d.span_last : 0u);
-    const uint32_t vspan = vblk >= 0 && vblk < d.nblocks
-                               ? (vblk < d.nblocks - 1 ? d.span_full : d.span_last)
-                               : 0u;
+    uint32_t kspan, vspan;
+    if constexpr (SPLIT) {
+      kspan = kblk >= d.jlo && kblk < d.jhi ? (kblk < d.nblocks - 1 ? d.span_full : d.span_last)
+                                            : 0u;
+      vspan = vblk >= d.jlo && vblk < d.jhi ? (vblk < d.nblocks - 1 ? d.span_full : d.span_last)
+                                            : 0u;
+    } else {  // the range is [0, nblocks); K blocks are never negative
+      kspan = kblk < d.nblocks - 1 ? d.span_full : (kblk == d.nblocks - 1 ? d.span_last : 0u);
+      vspan = vblk >= 0 && vblk < d.nblocks ? (vblk < d.nblocks - 1 ? d.span_full : d.span_last)
+                                            : 0u;
+    }
     const int kb = kspan ? kblk : 0, vb = vspan ? vblk : 0;  // keep addresses in range
     BlockDma b;
     b.k = block_rsrc<C::K_RB>(d.k, d, kb, kspan);
@@ -571,6 +581,10 @@ struct MfmaKernel {
 
   // ------------------------------------------------------------ kernel body
 
+  // SPLIT: split-KV work items (a key range of the tile, partial results
+  // to o_part / lse_part); without it the range is the whole tile and the
+  // split arithmetic folds away.
+  template <bool SPLIT>
   static __device__ void run(const AttnParams& p, char* smem) {
     __shared__ i32x4 s_item[2];
     const int tid = threadIdx.x;
@@ -617,12 +631,20 @@ struct MfmaKernel {
 
       const int n_kv = p.causal ? min(L, q0 + C::BM) : L;
       const int nblocks = (n_kv + C::BN - 1) / C::BN;
+      // this item's key blocks: split wi.split of num_splits (all of them
+      // without split-KV)
+      const int per = SPLIT ? (nblocks + p.num_splits - 1) / p.num_splits : nblocks;
+      const int jlo = SPLIT ? min(nblocks, wi.split * per) : 0;
+      const int jhi = SPLIT ? min(nblocks, jlo + per) : nblocks;
       // 32-key sub-tiles this wave computes (causal: keys up to wq0 + 31
       // only; none when all its rows are past the end); only the last can
       // need the mask
-      const int n_sub = wq0 >= L ? 0
-                        : p.causal ? min((L + 31) >> 5, (wq0 >> 5) + 1)
-                                   : (L + 31) >> 5;
+      const int n_sub_all = wq0 >= L ? 0
+                            : p.causal ? min((L + 31) >> 5, (wq0 >> 5) + 1)
+                                       : (L + 31) >> 5;
+      const int last_sub = n_sub_all - 1;                // the one that takes the mask
+      const int n_sub = SPLIT ? min(n_sub_all, 2 * jhi) : n_sub_all;  // sub-tiles 2 jlo .. n_sub - 1 here
+      const bool has_sub = n_sub > 2 * jlo;
       const int lim = p.causal ? min(L - 1, qi) : L - 1;  // last key visible to this lane
 
       // Q fragments (B operand): lane -> query qi, 8 (bf16) or 32 (fp8)
@@ -673,17 +695,22 @@ struct MfmaKernel {
       // apart anyway); with 4 K slots the last one goes out after the first
       // S.
       const int grp = wave >> 2;  // group 0 issues the DMA
-      const DmaSrc dsrc = dma_src(p, s0, L, g, nblocks);
-      auto blk = [&](int t) { return block_dma(dsrc, sbase, wave, t + C::KLEAD, t + 2); };
+      const DmaSrc dsrc = dma_src(p, s0, L, g, nblocks, jlo, jhi);
+      auto blk = [&](int t) {
+        return block_dma<SPLIT>(dsrc, sbase, wave, t + C::KLEAD, t + 2);
+      };
       if (grp == 0)
-        for (int t = -C::KLEAD; t < (C::KLEAD == 3 ? -1 : 0); ++t)
+        for (int t = jlo - C::KLEAD; t < jlo + (C::KLEAD == 3 ? -1 : 0); ++t)
           dma_ops<0, C::N_OPS>(blk(t), dl, junk, wave);
       wait_vm<0>();
       if (tid == 0) s_item[(it + 1) & 1] = nxt;
       __syncthreads();
-      if (n_sub > 0) s_tile(opaque(sbase + C::K_OFF + ln.k), opaque(sbase + C::R_OFF + ln.r), qf, w);
+      if (has_sub) {
+        const uint32_t ks0 = sbase + (uint32_t)(jlo % C::NKS) * C::KSLOT;
+        s_tile(opaque(ks0 + C::K_OFF + ln.k), opaque(ks0 + C::R_OFF + ln.r), qf, w);
+      }
       if constexpr (C::KLEAD == 3)
-        if (grp == 0) dma_ops<0, C::N_OPS>(blk(-1), dl, junk, wave);
+        if (grp == 0) dma_ops<0, C::N_OPS>(blk(jlo - 1), dl, junk, wave);
 
       // Per wave the sub-tiles run as alternating half-steps X_0 G_0 X_1
       // G_1 ...: X_i is sub-tile i's softmax (vector ALU), G_i its P V and
@@ -708,8 +735,8 @@ struct MfmaKernel {
         const float* ks =
             reinterpret_cast<const float*>(smem + (j % C::NKS) * C::KSLOT + C::KS_OFF) + 32 * H;
         if (!CHK || i < n_sub)
-          xphase<O0, O1, CHK>(w, ks, hf, cq, i == n_sub - 1, lim - 32 * i - 4 * hf, bd, dl, junk,
-                              wave);
+          xphase<O0, O1, CHK>(w, ks, hf, cq, SPLIT ? i == last_sub : i == n_sub - 1,
+                              lim - 32 * i - 4 * hf, bd, dl, junk, wave);
         else
           dma_ops<O0, O1>(bd, dl, junk, wave);
       };
@@ -751,15 +778,15 @@ struct MfmaKernel {
         if constexpr (GRP == 0) publish_block();
       };
       // blocks whose four half-steps all exist and need no mask, then the rest
-      const int n_steady = min(nblocks, n_sub > 0 ? (n_sub - 1) / 2 : 0);
+      const int j_steady = max(jlo, min(jhi, last_sub > 0 ? last_sub / 2 : 0));
       if (grp == 0) {
-        int j = 0;
-        for (; j < n_steady; ++j) block(P0{}, N{}, j);
-        for (; j < nblocks; ++j) block(P0{}, Y{}, j);
+        int j = jlo;
+        for (; j < j_steady; ++j) block(P0{}, N{}, j);
+        for (; j < jhi; ++j) block(P0{}, Y{}, j);
       } else {
-        int j = 0;
-        for (; j < n_steady; ++j) block(P1{}, N{}, j);
-        for (; j < nblocks; ++j) block(P1{}, Y{}, j);
+        int j = jlo;
+        for (; j < j_steady; ++j) block(P1{}, N{}, j);
+        for (; j < jhi; ++j) block(P1{}, Y{}, j);
       }
       // the last batches requested nothing; drain, and let group 1 finish
       // its last products, before the rings are reused for the output
@@ -770,6 +797,27 @@ struct MfmaKernel {
       // ---- epilogue
       const float lt = half_sum(w.l);
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      if constexpr (SPLIT) {
+        // split-KV partial: float32 O over this item's key range (zero where
+        // the range holds no visible key) and its LSE (-inf there), straight
+        // from the registers: each lane writes 16-byte runs of its row
+        if (qvalid && s0 + qi < p.part_tokens) {
+          const size_t prow = ((size_t)wi.split * p.part_tokens + s0 + qi) * p.num_heads + wi.h;
+          float* dst = p.o_part + prow * C::DV;
+#pragma unroll
+          for (int t = 0; t < C::DV_TILES; ++t)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+              const f32x4 x = {w.o[t][4 * a4 + 0] * inv, w.o[t][4 * a4 + 1] * inv,
+                               w.o[t][4 * a4 + 2] * inv, w.o[t][4 * a4 + 3] * inv};
+              *reinterpret_cast<f32x4*>(dst + t * 32 + 8 * a4 + 4 * hf) = x;
+            }
+          if (hf == 0)
+            p.lse_part[((size_t)wi.split * p.num_heads + wi.h) * p.part_tokens + s0 + qi] =
+                lt > 0.f ? (w.m + log2f(lt)) * kLn2 : -INFINITY;
+        }
+        continue;
+      }
       char* ost = smem + wave * 32 * C::O_ROW + lane32 * C::O_ROW;
 #pragma unroll
       for (int t = 0; t < C::DV_TILES; ++t)
@@ -800,15 +848,16 @@ struct MfmaKernel {
   }
 };
 
-template <class C>
+template <class C, bool SPLIT>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void attn_fwd_mfma_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-  MfmaKernel<C>::run(p, smem);
+  MfmaKernel<C>::template run<SPLIT>(p, smem);
 }
 
-template <class C>
+template <class C, bool SPLIT = false>
 hipError_t launch_mfma(const AttnParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_fwd_mfma_kernel<C>, dim3(grid), dim3(C::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_mfma_kernel<C, SPLIT>), dim3(grid), dim3(C::THREADS), 0, stream,
+                     p);
   return hipGetLastError();
 }
 
@@ -816,7 +865,7 @@ template <class C>
 int blocks_mfma() {
   static int cached = [] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_mfma_kernel<C>, C::THREADS,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_fwd_mfma_kernel<C, false>, C::THREADS,
                                                      0) != hipSuccess ||
         n < 1)
       n = 1;

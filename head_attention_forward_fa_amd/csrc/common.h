@@ -21,16 +21,21 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // A work item of the persistent scheduler: query tile qt of query head h
-// over sequence b, whose tokens are s0 .. s0 + L - 1.  A table entry is the
-// 16-byte vector {s0, L, (h << 20) | qt, b}; L = -1 marks "no work left".
+// over sequence b, whose tokens are s0 .. s0 + L - 1, against key split
+// `split` of the tile's keys (split-KV; 0 when the keys are not split).  A
+// table entry is the 16-byte vector {s0, L, (h << 20) | qt, (split << 24) |
+// b}; L = -1 marks "no work left".
 struct WorkItem {
-  int s0, L, h, qt, b;
+  int s0, L, h, qt, b, split;
 };
 __device__ __forceinline__ WorkItem decode_item(const i32x4& e) {
-  return WorkItem{e[0], e[1], (int)((unsigned)e[2] >> 20), e[2] & 0xFFFFF, e[3]};
+  return WorkItem{e[0], e[1], (int)((unsigned)e[2] >> 20), e[2] & 0xFFFFF, e[3] & 0xFFFFFF,
+                  (int)((unsigned)e[3] >> 24)};
 }
 constexpr int kMaxQTilesPerSeq = 1 << 20;
 constexpr int kMaxHeads = 1 << 11;
+constexpr int kMaxBatch = 1 << 24;
+constexpr int kMaxSplits = 64;
 
 // Scheduler state kept in device memory (the library workspace).  Each
 // queue (one per XCD) sits on its own 256-byte line, so that the atomic
@@ -72,6 +77,15 @@ struct AttnParams {
   int group;          // num_heads / num_kv_heads
   int causal;
   float scale_log2;   // sigma * log2(e)
+  // split-KV: the keys of every query tile are cut into num_splits ranges
+  // of whole key blocks; with o_part set, a work item writes its range's
+  // partial result (float32 O normalised over the range, and its LSE) to
+  // o_part [num_splits, T, Hq, Dv] / lse_part [num_splits, Hq, T] instead of
+  // o / lse.
+  int num_splits;
+  int part_tokens;    // T of the partial layouts (rows past it are not written)
+  float* o_part;
+  float* lse_part;
 };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

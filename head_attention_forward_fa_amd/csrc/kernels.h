@@ -16,8 +16,8 @@ constexpr int kBlockM_F32 = 64;
 constexpr int kBlockN_F32 = 32;
 
 hipError_t launch_prepass(const int32_t* cu, int batch, int num_heads, int num_kv_heads,
-                          int causal, int bm, int bn, int capacity, i32x4* table,
-                          SchedState* st, int* scratch, hipStream_t stream);
+                          int causal, int bm, int bn, int num_splits, int capacity,
+                          i32x4* table, SchedState* st, int* scratch, hipStream_t stream);
 
 hipError_t launch_sched_visit(int batch, int num_heads, int tiles, const i32x4* table,
                               SchedState* st, int* visits, int grid,
@@ -28,6 +28,12 @@ hipError_t launch_sched_visit(int batch, int num_heads, int tiles, const i32x4* 
 hipError_t launch_fp8_quant(const void* x, bool bf16, int64_t rows, int cols, uint8_t* codes,
                             float* scales, hipStream_t stream);
 
+// Split-KV merge (combine.hip): o_part [num_splits, T, H, Dv] float32 and
+// lse_part [num_splits, H, T] -> o [T, H, Dv] (bf16 or float32), lse [H, T].
+hipError_t launch_combine(const float* o_part, const float* lse_part, int num_splits, int T,
+                          int H, int dv, bool bf16_out, void* o, float* lse,
+                          hipStream_t stream);
+
 // A kernel variant: its launcher and its occupancy (resident workgroups per
 // CU at its LDS and register footprint, computed once per device).
 struct Variant {
@@ -36,6 +42,8 @@ struct Variant {
   int block_m;
   int block_n;
   int lds_bytes;
+  // split-KV instantiation (partial results per key range); null if none
+  hipError_t (*launch_split)(const AttnParams& p, int grid, hipStream_t stream);
 };
 
 // Lookup of the compiled variant for (dtype, Dn, Dr, Dv); nullptr if none.

@@ -11,7 +11,8 @@
 // version:
 //
 //   * a one-workgroup prepass turns cu_seqlens into a table of work items
-//     {s0, L, h, q-tile, b}.  Items are grouped by (sequence, KV head), so
+//     {s0, L, h, q-tile, b} (times the key splits under split-KV: one item
+//     per split, next to each other).  Items are grouped by (sequence, KV head), so
 //     that the query heads sharing a KV head and every q-tile of that
 //     sequence sit next to each other; groups are dealt to 8 queues, one per
 //     XCD, largest first in a snake order so the queues carry equal work;
@@ -48,8 +49,8 @@ __device__ __forceinline__ int snake_bin(int r) {
 
 __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
     const int32_t* __restrict__ cu, int batch, int num_heads, int num_kv_heads, int causal,
-    int bm, int bn, int capacity, i32x4* __restrict__ table, SchedState* __restrict__ st,
-    int* __restrict__ scratch) {
+    int bm, int bn, int num_splits, int capacity, i32x4* __restrict__ table,
+    SchedState* __restrict__ st, int* __restrict__ scratch) {
   __shared__ long long s_cost[kSortedMax];
   __shared__ int s_items[kSortedMax];   // group -> item count
   __shared__ int s_irank[kSortedMax];   // rank -> item count
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
     const int L = cu[b + 1] - cu[b];
     const int nqt = L > 0 ? (L + bm - 1) / bm : 0;
     if (L < 0 || nqt >= kMaxQTilesPerSeq) s_bad = 1;
-    const int items = nqt * group;
+    const int items = nqt * group * num_splits;
     my_items += items;
     if (sorted) {
       s_cost[i] = group_cost(L, bm, bn, causal) * group;
@@ -199,7 +200,8 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
     }
     for (int qt = nqt - 1; qt >= 0; --qt)
       for (int hh = 0; hh < group; ++hh)
-        table[pos++] = i32x4{s0, L, ((g * group + hh) << 20) | qt, b};
+        for (int sp = 0; sp < num_splits; ++sp)
+          table[pos++] = i32x4{s0, L, ((g * group + hh) << 20) | qt, (sp << 24) | b};
   }
 }
 
@@ -234,10 +236,11 @@ __global__ __launch_bounds__(256) void sched_visit_kernel(int batch, int num_hea
 }  // namespace
 
 hipError_t launch_prepass(const int32_t* cu, int batch, int num_heads, int num_kv_heads,
-                          int causal, int bm, int bn, int capacity, i32x4* table,
-                          SchedState* st, int* scratch, hipStream_t stream) {
+                          int causal, int bm, int bn, int num_splits, int capacity,
+                          i32x4* table, SchedState* st, int* scratch, hipStream_t stream) {
   hipLaunchKernelGGL(sched_prepass_kernel, dim3(1), dim3(kPrepassThreads), 0, stream, cu, batch,
-                     num_heads, num_kv_heads, causal, bm, bn, capacity, table, st, scratch);
+                     num_heads, num_kv_heads, causal, bm, bn, num_splits, capacity, table, st,
+                     scratch);
   return hipGetLastError();
 }
 

@@ -50,8 +50,17 @@ def mha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
             k_scale: Optional[torch.Tensor] = None,
             softmax_scale: Optional[float] = None,
             out: Optional[torch.Tensor] = None,
-            lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+            lse: Optional[torch.Tensor] = None,
+            num_splits: int = 1,
+            o_partial: Optional[torch.Tensor] = None,
+            lse_partial: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Fused attention forward; returns (o, lse).
+
+    num_splits > 1 runs mha_fwd_splitkv: the keys of every query tile are cut
+    into that many ranges run as separate work items, then merged
+    (mha_combine_splits); o_partial [num_splits, T, Hq, Dv] and lse_partial
+    [num_splits, Hq, T] float32 are its scratch (allocated when not given;
+    they hold the per-split partial results afterwards).
 
     q [T, Hq, Dn], k [T, Hkv, Dn], v [T, Hkv, Dv] with cu_seqlens (int32
     [B+1], on the device) and max_seqlen; or q [B, S, Hq, Dn] etc. for a dense
@@ -100,13 +109,25 @@ def mha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     _need(lse_t, "lse", dev, torch.float32, (Hq, T))
     stream = torch.cuda.current_stream(dev).cuda_stream
     lib = nat.load()
+    scale_arg = float(softmax_scale) if softmax_scale is not None else 0.0
     with torch.cuda.device(dev):
-        st = lib.mha_fwd(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(o), _ptr(lse_t),
-                         _ptr(cu), int(B), int(max_seqlen), int(Hq), int(Hkv),
-                         int(Dn), int(Dr), int(Dv), _ptr(qrf), _ptr(krf),
-                         int(bool(causal)),
-                         float(softmax_scale) if softmax_scale is not None else 0.0,
-                         code, _ptr(qsf), _ptr(ksf), stream)
+        if num_splits == 1 and o_partial is None and lse_partial is None:
+            st = lib.mha_fwd(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(o), _ptr(lse_t),
+                             _ptr(cu), int(B), int(max_seqlen), int(Hq), int(Hkv),
+                             int(Dn), int(Dr), int(Dv), _ptr(qrf), _ptr(krf),
+                             int(bool(causal)), scale_arg, code, _ptr(qsf), _ptr(ksf), stream)
+        else:
+            op = o_partial if o_partial is not None else torch.empty(
+                (num_splits, T, Hq, Dv), dtype=torch.float32, device=dev)
+            lp = lse_partial if lse_partial is not None else torch.empty(
+                (num_splits, Hq, T), dtype=torch.float32, device=dev)
+            _need(op, "o_partial", dev, torch.float32, (num_splits, T, Hq, Dv))
+            _need(lp, "lse_partial", dev, torch.float32, (num_splits, Hq, T))
+            st = lib.mha_fwd_splitkv(_ptr(qf), _ptr(kf), _ptr(vf), _ptr(o), _ptr(lse_t),
+                                     _ptr(cu), int(B), int(max_seqlen), int(Hq), int(Hkv),
+                                     int(Dn), int(Dr), int(Dv), _ptr(qrf), _ptr(krf),
+                                     int(bool(causal)), scale_arg, code, _ptr(qsf), _ptr(ksf),
+                                     int(T), int(num_splits), _ptr(op), _ptr(lp), stream)
     nat.check(st)
     if dense:
         o = o.view(B, S, Hq, Dv)
@@ -175,3 +196,35 @@ def mha_quantize_fp8(x: torch.Tensor, *, codes: Optional[torch.Tensor] = None,
                                          stream)
     nat.check(st)
     return c, s
+
+
+def mha_combine_splits(o_partial: torch.Tensor, lse_partial: torch.Tensor, *,
+                       out_dtype: torch.dtype = torch.bfloat16,
+                       out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Log-sum-exp merge of partial results (mha_combine_splits of the C ABI).
+
+    o_partial [n, T, H, Dv] and lse_partial [n, H, T] float32 on a GPU;
+    returns o [T, H, Dv] (out_dtype: bfloat16 or float32) and lse [H, T].
+    """
+    if o_partial.dim() != 4 or lse_partial.dim() != 3:
+        raise ValueError("o_partial must be [n, T, H, Dv] and lse_partial [n, H, T]")
+    n, T, H, Dv = o_partial.shape
+    dev = o_partial.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    _need(o_partial, "o_partial", dev, torch.float32)
+    _need(lse_partial, "lse_partial", dev, torch.float32, (n, H, T))
+    o = out if out is not None else torch.empty((T, H, Dv), dtype=out_dtype, device=dev)
+    _need(o, "out", dev, out_dtype, (T, H, Dv))
+    lse_t = lse if lse is not None else torch.empty((H, T), dtype=torch.float32, device=dev)
+    _need(lse_t, "lse", dev, torch.float32, (H, T))
+    code = nat.MHA_DTYPE_BF16 if out_dtype == torch.bfloat16 else nat.MHA_DTYPE_F32
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = nat.load().mha_combine_splits(_ptr(o_partial), _ptr(lse_partial), int(n), int(T),
+                                           int(H), int(Dv), code, _ptr(o), _ptr(lse_t), stream)
+    nat.check(st)
+    return o, lse_t

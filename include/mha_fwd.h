@@ -173,6 +173,71 @@ int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen
                     int32_t block_m, int32_t grid, int32_t* visits, void* stream);
 
 /*
+ * mha_fwd_splitkv -- mha_fwd with the keys of every query tile cut into
+ * num_splits ranges that run as separate work items, merged afterwards (more
+ * work items when batch x heads x query tiles would leave compute units
+ * idle).  The pages name the split count (SM100AttentionSMem, comptime
+ * members: MiscMBarsType is built with the config's splitk_partitions) and
+ * keep per-row softmax statistics (Methods: correction_smem); how the keys
+ * are cut and merged is this library's:
+ *
+ *   - a query tile (256 rows) of sequence b sees nb = ceil(n / 64) key blocks
+ *     of 64, n = min(L_b, 256 (qt + 1)) when causal, else L_b; split s of
+ *     num_splits holds blocks [s p, min((s + 1) p, nb)), p = ceil(nb /
+ *     num_splits) (possibly none);
+ *   - each split writes its partial result for every row r of the tile:
+ *     lse_partial[s, h, r] = ln sum_j exp(S[r, j]) and o_partial[s, r, h, :] =
+ *     sum_j exp(S[r, j] - lse_partial[s, h, r]) v[j, g, :] over the visible keys
+ *     j of the split (o 0, lse -inf when there are none);
+ *   - mha_combine_splits then writes o and lse (bf16 o for BF16 / FP8).
+ *
+ * Arguments as for mha_fwd, plus:
+ *   total_tokens  T = cu_seqlens[batch] (the caller's token count; the partial
+ *                 layouts use it; rows at or past it are not written)
+ *   num_splits    1 .. 64 (1: exactly mha_fwd, the partials are not used)
+ *   o_partial     device float32 [num_splits, T, num_heads, v_dim], 16-byte
+ *                 aligned, caller-owned scratch (written)
+ *   lse_partial   device float32 [num_splits, num_heads, T] (written)
+ * BF16 and FP8_E4M3 shapes only (F32: MHA_ERR_UNSUPPORTED).  Errors as for
+ * mha_fwd; also MHA_ERR_INVALID_ARG for num_splits outside 1 .. 64, a
+ * negative total_tokens, or NULL / misaligned partial buffers with
+ * num_splits > 1.  The kernel-events hook brackets the attention kernel;
+ * the merge follows it on the same stream.
+ */
+int mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim_nope,
+                    int32_t head_dim_rope, int32_t v_dim, const void* q_rope, const void* k_rope,
+                    int32_t causal, float softmax_scale, int32_t dtype, const float* q_scale,
+                    const float* k_scale, int32_t total_tokens, int32_t num_splits,
+                    float* o_partial, float* lse_partial, void* stream);
+
+/*
+ * mha_combine_splits -- the log-sum-exp merge of partial attention results
+ * over disjoint key sets (the second half of mha_fwd_splitkv; also merges
+ * results computed elsewhere, e.g. on several devices):
+ *
+ *   lse[h, t] = ln sum_s exp(lse_partial[s, h, t])
+ *   o[t, h, :] = sum_s exp(lse_partial[s, h, t] - lse[h, t]) o_partial[s, t, h, :]
+ *
+ * with the largest term factored out; a partial with lse -inf weighs 0; a
+ * row whose partials are all -inf gets o = 0, lse = -inf.
+ *   o_partial    device float32 [num_splits, total_tokens, num_heads, v_dim],
+ *                16-byte aligned
+ *   lse_partial  device float32 [num_splits, num_heads, total_tokens]
+ *   o            device [total_tokens, num_heads, v_dim], float32 (out_dtype
+ *                MHA_DTYPE_F32) or bfloat16 (MHA_DTYPE_BF16, RNE), 16-byte
+ *                aligned (written)
+ *   lse          device float32 [num_heads, total_tokens] (written)
+ * num_splits 1 .. 64, v_dim 64 or 128 (else MHA_ERR_UNSUPPORTED).
+ * HBM-bound: reads num_splits x (v_dim x 4 + 4), writes v_dim x {4, 2} + 4
+ * bytes per (token, head).
+ */
+int mha_combine_splits(const float* o_partial, const float* lse_partial, int32_t num_splits,
+                       int32_t total_tokens, int32_t num_heads, int32_t v_dim, int32_t out_dtype,
+                       void* o, float* lse, void* stream);
+
+/*
  * mha_quantize_fp8 -- per-token fp8 quantisation of Q or K rows, the step in
  * front of the FP8_E4M3 path (whose Q and K are E4M3 codes with one float32
  * scale per token and head: SM100AttentionSMem, Parameters: scale_dtype_;

@@ -168,6 +168,15 @@ WORKLOADS = {
 
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# Workloads of the "next" rows: a long causal sequence over few heads, whose
+# 256 query tiles (4 heads x 64) leave most compute units idle for most of
+# the run unless the keys are split (split-KV).
+EXTRA_WORKLOADS = {
+    "bf16_causal_b1_h4_s16384_d128": dict(
+        dtype="bf16", seqlens=[16384], num_heads=4, num_kv_heads=4,
+        head_dim_nope=128, v_dim=128, causal=True),
+}
+
 
 def ragged_lengths(rng: np.random.Generator, n: int = 16, lo: int = 64, hi: int = 8192):
     return rng.integers(lo, hi + 1, size=n)
@@ -175,7 +184,7 @@ def ragged_lengths(rng: np.random.Generator, n: int = 16, lo: int = 64, hi: int 
 
 def workload(name: str, seed: int = 0) -> Inputs:
     """The named workload's inputs, drawn from `seed`."""
-    spec = dict(WORKLOADS[name])
+    spec = dict(WORKLOADS[name] if name in WORKLOADS else EXTRA_WORKLOADS[name])
     rng = np.random.default_rng(seed)
     if spec["seqlens"] == "ragged16":
         spec["seqlens"] = ragged_lengths(rng)
@@ -204,3 +213,20 @@ def make_rows(shape, *, dtype: str = "bf16", seed: int = 0,
     mag = rng.lognormal(0.0, magnitude_sigma, size=tuple(shape[:-1]) + (1,)).astype(np.float32)
     x = (x * mag).astype(np.float32)
     return x if dtype == "f32" else to_bf16_bits(x)
+
+
+def make_partials(num_splits: int, total_tokens: int, num_heads: int, v_dim: int, *,
+                  seed: int = 0, empty_fraction: float = 0.2):
+    """Random partial results for the split merge: o_partial float32
+    [n, T, H, Dv] ~ N(0,1) and lse_partial float32 [n, H, T] ~ N(0, 4), with
+    about empty_fraction of the (split, head, token) entries set to an empty
+    partial (o 0, lse -inf), including whole rows with every split empty."""
+    rng = np.random.default_rng(seed)
+    o = _normal(rng, (num_splits, total_tokens, num_heads, v_dim))
+    lse = (_normal(rng, (num_splits, num_heads, total_tokens)) * 2.0).astype(np.float32)
+    empty = rng.random((num_splits, num_heads, total_tokens)) < empty_fraction
+    if total_tokens > 1:
+        empty[:, :, total_tokens // 2] = True  # a row with every split empty
+    lse[empty] = -np.inf
+    o[np.transpose(empty, (0, 2, 1))] = 0.0
+    return o, lse

@@ -114,3 +114,28 @@ def sample_tokens(inp: Inputs, n_random: int = 24, seed: int = 1):
 
 def max_abs(a, b):
     return float(np.max(np.abs(np.asarray(a) - np.asarray(b)))) if np.size(a) else 0.0
+
+
+def split_key_ranges(cu_seqlens, causal: bool, num_splits: int, block_m: int = 256,
+                     block_n: int = 64):
+    """lo, hi int arrays [num_splits, T]: the key range (local indices) of
+    each split for every query token, by the rule mha_fwd_splitkv documents:
+    a query tile of block_m rows sees nb = ceil(n / block_n) key blocks (n =
+    min(L, block_m (qt + 1)) causal, else L); split s holds blocks
+    [s p, min((s + 1) p, nb)), p = ceil(nb / num_splits)."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T = int(cu[-1])
+    lo = np.zeros((num_splits, T), np.int64)
+    hi = np.zeros((num_splits, T), np.int64)
+    for b in range(len(cu) - 1):
+        L = int(cu[b + 1] - cu[b])
+        for i in range(L):
+            qt = i // block_m
+            n = min(L, block_m * (qt + 1)) if causal else L
+            nb = -(-n // block_n)
+            p = -(-nb // num_splits)
+            for s in range(num_splits):
+                b0, b1 = min(nb, s * p), min(nb, (s + 1) * p)
+                lo[s, cu[b] + i] = b0 * block_n
+                hi[s, cu[b] + i] = b1 * block_n
+    return lo, hi

@@ -1,0 +1,121 @@
+"""Split-KV (mha_fwd_splitkv) and the merge (mha_combine_splits) on the GPU
+against the oracle, through the C ABI.
+
+* merged O / LSE against the full oracle at mha_fwd's tolerances: causal and
+  not, ragged with an empty and a one-token sequence, GQA, D64, rope, fp8,
+  split counts from 2 to more than some tiles have blocks (empty splits);
+* the partial results themselves against the oracle's attention over each
+  split's key range (the documented rule), empty splits exactly O 0 / -inf;
+* num_splits = 1 is mha_fwd bit for bit; runs repeat bit for bit;
+* the merge alone on seeded random partials (with empty ones and all-empty
+  rows) against the oracle's merge, float32 and bf16 output;
+* the split-KV measurement workload (causal B1 H4 S16384 D128, 4 splits) at
+  full size on sampled rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mha_inputs as mi
+from _util import (TOL_LSE, TOL_O, decoded, device_tensors, max_abs, oracle_full, oracle_rows,
+                   sample_tokens, split_key_ranges, to_f64)
+from oracle import splitkv as osk
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # dtype, lengths, Hq, Hkv, Dn, Dr, Dv, causal, num_splits
+    ("bf16", [1100], 2, 2, 128, 0, 128, True, 2),
+    ("bf16", [1100], 2, 2, 128, 0, 128, True, 4),
+    ("bf16", [1100, 31], 2, 1, 128, 0, 128, False, 3),
+    ("bf16", [1, 129, 0, 517, 64], 8, 2, 128, 0, 128, True, 3),
+    ("bf16", [200, 77], 4, 1, 64, 0, 64, True, 5),
+    ("bf16", [650], 2, 2, 128, 64, 128, True, 2),
+    ("fp8", [900, 40], 2, 2, 128, 0, 128, True, 4),
+    ("fp8", [300], 4, 2, 128, 0, 128, False, 2),
+]
+
+
+def _inputs(dtype, lens, hq, hkv, dn, dr, dv, causal, seed=3):
+    return mi.make_inputs(dtype=dtype, seqlens=lens, num_heads=hq, num_kv_heads=hkv,
+                          head_dim_nope=dn, head_dim_rope=dr, v_dim=dv, causal=causal, seed=seed,
+                          name=f"{dtype}-{lens}")
+
+
+def _run(inp, t, num_splits, o_partial=None, lse_partial=None):
+    from head_attention_forward_fa_amd import mha_fwd
+    o, lse = mha_fwd(t["q"], t["k"], t["v"], causal=inp.causal, cu_seqlens=t["cu_seqlens"],
+                     max_seqlen=inp.max_seqlen, q_rope=t["q_rope"], k_rope=t["k_rope"],
+                     q_scale=t["q_scale"], k_scale=t["k_scale"], num_splits=num_splits,
+                     o_partial=o_partial, lse_partial=lse_partial)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-{c[1]}-s{c[8]}-{'c' if c[7] else 'n'}")
+def test_merged_and_partials_match_oracle(case):
+    dtype, lens, hq, hkv, dn, dr, dv, causal, ns = case
+    inp = _inputs(dtype, lens, hq, hkv, dn, dr, dv, causal)
+    t = device_tensors(inp)
+    T = inp.total_tokens
+    op = torch.empty((ns, T, hq, dv), dtype=torch.float32, device="cuda")
+    lp = torch.empty((ns, hq, T), dtype=torch.float32, device="cuda")
+    o, lse = _run(inp, t, ns, op, lp)
+    ref_o, ref_l = oracle_full(inp)
+    eo, el = max_abs(to_f64(o), ref_o), max_abs(to_f64(lse), ref_l)
+    assert eo <= TOL_O[dtype], f"merged O max-abs {eo}"
+    assert el <= TOL_LSE, f"merged LSE max-abs {el}"
+    # the partials: attention over each split's key range
+    q, k, v, qr, kr = decoded(inp)
+    lo, hi = split_key_ranges(inp.cu_seqlens, causal, ns)
+    opn, lpn = to_f64(op), to_f64(lp)
+    for s in range(ns):
+        po, pl = osk.mha_forward_key_range(q, k, v, inp.cu_seqlens, causal, lo[s], hi[s],
+                                           inp.softmax_scale, q_rope=qr, k_rope=kr)
+        empty = np.isneginf(pl)
+        assert np.array_equal(np.isneginf(lpn[s]), empty), f"split {s}: empty rows differ"
+        assert np.all(opn[s][np.transpose(empty)] == 0.0)
+        ok = ~empty
+        assert max_abs(lpn[s][ok], pl[ok]) <= TOL_LSE, f"split {s} LSE"
+        okt = np.transpose(ok)
+        assert max_abs(opn[s][okt], po[okt]) <= TOL_O[dtype], f"split {s} O"
+
+
+def test_one_split_is_mha_fwd_and_runs_repeat():
+    inp = _inputs("bf16", [1, 129, 0, 517, 64], 8, 2, 128, 0, 128, True)
+    t = device_tensors(inp)
+    o1, l1 = _run(inp, t, 1)
+    o2, l2 = _run(inp, t, 1, torch.empty((1, inp.total_tokens, 8, 128), device="cuda"),
+                  torch.empty((1, 8, inp.total_tokens), device="cuda"))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    a = _run(inp, t, 3)
+    b = _run(inp, t, 3)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("n,T,H,D", [(1, 5, 2, 64), (3, 301, 4, 128), (8, 77, 3, 64)])
+def test_merge_alone_matches_oracle(out_dtype, n, T, H, D):
+    from head_attention_forward_fa_amd import mha_combine_splits
+    op, lp = mi.make_partials(n, T, H, D, seed=n * 100 + T)
+    o, l = mha_combine_splits(torch.from_numpy(op).cuda(), torch.from_numpy(lp).cuda(),
+                              out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ro, rl = osk.merge_partials(op, lp)
+    l64 = to_f64(l)
+    assert np.array_equal(np.isneginf(l64), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    assert max_abs(l64[fin], rl[fin]) <= 1e-5
+    tol = 1e-5 if out_dtype == torch.float32 else 2e-2
+    assert max_abs(to_f64(o), ro) <= tol
+
+
+def test_splitkv_workload_full_size_sampled():
+    inp = mi.workload("bf16_causal_b1_h4_s16384_d128")
+    t = device_tensors(inp)
+    o, lse = _run(inp, t, 4)
+    toks = sample_tokens(inp, 40, seed=1)
+    ref_o, ref_l = oracle_rows(inp, toks)
+    assert max_abs(to_f64(o)[toks], ref_o) <= TOL_O["bf16"]
+    assert max_abs(to_f64(lse)[:, toks], ref_l) <= TOL_LSE
