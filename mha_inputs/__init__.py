@@ -110,9 +110,9 @@ def make_inputs(*, dtype: str, seqlens, num_heads: int, num_kv_heads: int,
                 fp8_magnitude_sigma: float = 0.5) -> Inputs:
     """Draw one problem: i.i.d. N(0,1) elements, packed along tokens.
 
-    fp8: Q/K rows are N(0,1) vectors times a per-token lognormal(0, sigma)
-    magnitude (one per token, shared by its heads), then quantised per
-    (token, head) row; V stays bfloat16.
+    fp8: Q/K nope rows are N(0,1) vectors times a per-token lognormal(0,
+    sigma) magnitude (one per token, shared by its heads), then quantised per
+    (token, head) row; a rope part and V stay bfloat16.
     """
     if dtype not in ("f32", "bf16", "fp8"):
         raise ValueError(dtype)
@@ -135,13 +135,14 @@ def make_inputs(*, dtype: str, seqlens, num_heads: int, num_kv_heads: int,
                    q_rope=None if qr is None else to_bf16_bits(qr),
                    k_rope=None if kr is None else to_bf16_bits(kr))
     else:
-        if head_dim_rope:
-            raise ValueError("fp8 inputs carry no rope part")
         mq = rng.lognormal(0.0, fp8_magnitude_sigma, size=(T, 1, 1)).astype(np.float32)
         mk = rng.lognormal(0.0, fp8_magnitude_sigma, size=(T, 1, 1)).astype(np.float32)
         q8, qs = to_e4m3_per_row(qn * mq)
         k8, ks = to_e4m3_per_row(kn * mk)
-        out.update(q=q8, k=k8, v=to_bf16_bits(vv), q_scale=qs, k_scale=ks)
+        # a rope part stays bfloat16 (its own element type, unscaled)
+        out.update(q=q8, k=k8, v=to_bf16_bits(vv), q_scale=qs, k_scale=ks,
+                   q_rope=None if qr is None else to_bf16_bits(qr),
+                   k_rope=None if kr is None else to_bf16_bits(kr))
     return Inputs(**out)
 
 
@@ -172,6 +173,10 @@ WORKLOAD_ORDER = list(WORKLOADS)
 # 256 query tiles (4 heads x 64) leave most compute units idle for most of
 # the run unless the keys are split (split-KV).
 EXTRA_WORKLOADS = {
+    # fp8 nope + bf16 rope: the rope workload's shape with an 8-bit nope part
+    "fp8_nope128_rope64_causal_b2_h16_s8192": dict(
+        dtype="fp8", seqlens=[8192] * 2, num_heads=16, num_kv_heads=16,
+        head_dim_nope=128, head_dim_rope=64, v_dim=128, causal=True),
     "bf16_causal_b1_h4_s16384_d128": dict(
         dtype="bf16", seqlens=[16384], num_heads=4, num_kv_heads=4,
         head_dim_nope=128, v_dim=128, causal=True),

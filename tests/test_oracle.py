@@ -327,6 +327,28 @@ def test_fp8_equals_attention_on_dequantised_values():
     assert np.allclose(o, ob, atol=1e-12) and np.allclose(lse, lb, atol=1e-12)
 
 
+def test_fp8_nope_bf16_rope_scale_covers_the_nope_part_only():
+    # reading of the mixed split: the per-token scales multiply the nope
+    # product only; the rope part adds its bf16 dot product unscaled
+    inp = make_inputs(dtype="fp8", seqlens=[11, 4], num_heads=2, num_kv_heads=1,
+                      head_dim_nope=16, head_dim_rope=8, v_dim=8, causal=True, seed=4)
+    q = oracle.dequantize_per_token(inp.q, inp.q_scale)
+    k = oracle.dequantize_per_token(inp.k, inp.k_scale)
+    qr, kr = oracle.decode_bf16(inp.q_rope), oracle.decode_bf16(inp.k_rope)
+    v = oracle.decode_bf16(inp.v)
+    o, lse = oracle.mha_forward(q, k, v, inp.cu_seqlens, True, q_rope=qr, k_rope=kr)
+    tq = (torch.from_numpy(inp.q).view(torch.float8_e4m3fn).double()
+          * torch.from_numpy(inp.q_scale).double()[..., None]).numpy()
+    tk = (torch.from_numpy(inp.k).view(torch.float8_e4m3fn).double()
+          * torch.from_numpy(inp.k_scale).double()[..., None]).numpy()
+    ob, lb = brute_force(tq, tk, v, inp.cu_seqlens, True, 1 / math.sqrt(24.0), qr, kr)
+    assert np.allclose(o, ob, atol=1e-12) and np.allclose(lse, lb, atol=1e-12)
+    # the rope part really is unscaled: scaling it by q_scale changes the result
+    ob2, _ = brute_force(tq, tk, v, inp.cu_seqlens, True, 1 / math.sqrt(24.0),
+                         qr * inp.q_scale[..., None], kr)
+    assert not np.allclose(o, ob2, atol=1e-6)
+
+
 def test_rows_entry_matches_full_oracle():
     rng = np.random.default_rng(18)
     lens = [6, 9]
