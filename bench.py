@@ -129,9 +129,10 @@ class HipEvents:
 
 def peak_for(inp) -> float:
     if inp.dtype == "fp8":
-        # QK^T runs at the fp8 rate, PV at the bf16 rate: time-weighted peak
-        dqk, dv = inp.head_dim_nope, inp.v_dim
-        return (dqk + dv) / (dqk / PEAK_TFLOPS["fp8"] + dv / PEAK_TFLOPS["bf16"])
+        # the nope QK^T runs at the fp8 rate, a rope QK^T and PV at the bf16
+        # rate: time-weighted peak
+        dn, dr, dv = inp.head_dim_nope, inp.head_dim_rope, inp.v_dim
+        return (dn + dr + dv) / (dn / PEAK_TFLOPS["fp8"] + (dr + dv) / PEAK_TFLOPS["bf16"])
     return PEAK_TFLOPS[inp.dtype]
 
 

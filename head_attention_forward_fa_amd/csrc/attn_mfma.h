@@ -79,6 +79,9 @@ template <int DN_, int DR_, int DV_, bool FP8_>
 struct MfmaCfg {
   static constexpr int DN = DN_, DR = DR_, DV = DV_;
   static constexpr bool FP8 = FP8_;
+  // fp8 nope with a bfloat16 rope part: the per-token scales multiply the
+  // nope product only, so the two products accumulate separately
+  static constexpr bool MIXED = FP8 && DR > 0;
   static constexpr int BM = kBlockM_Mfma;  // 256 query rows per item
   static constexpr int BN = kBlockN_Mfma;  // 64 keys per block
   static constexpr int WAVES = BM / 32;    // 8 waves, two per SIMD
@@ -129,7 +132,6 @@ struct MfmaCfg {
   static constexpr int V_DMA = V_INST / DW;
   static constexpr int N_OPS = K_DMA + R_DMA + KS_DMA + V_DMA;
 
-  static_assert(!FP8 || DR == 0, "fp8 Q/K carry no rope part");
   static_assert(K_RB == 128 || K_RB == 256, "K rows of 128 or 256 bytes");
   static_assert(DR == 0 || R_RB == 128, "rope rows of 128 bytes");
   static_assert(V_RB == 128 || V_RB == 256, "V rows of 128 or 256 bytes");
@@ -429,6 +431,13 @@ struct MfmaKernel {
           lp(rt) + 32 * (s - C::QK_STEPS));
     }
   }
+  // A operand of rope step s of the mixed layout (bf16 rows at pitch R_RP)
+  static __device__ __forceinline__ bf16x8 r_frag(uint32_t rt, int s) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(lp(rt) + 32 * s);
+  }
+  static __device__ __forceinline__ f32x16 r_mfma(const bf16x8& a, const bf16x8& b, f32x16 acc) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+  }
   static __device__ __forceinline__ f32x16 s_mfma(const QFrag& a, const QFrag& b, f32x16 acc) {
     if constexpr (C::FP8)
       return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
@@ -460,6 +469,7 @@ struct MfmaKernel {
   struct State {
     f32x16 o[C::DV_TILES];  // O^T accumulator (lane = query, 16 dv rows per tile)
     f32x16 st;              // S^T of the sub-tile awaiting its softmax half-step
+    f32x16 sr;              // its rope part (mixed layout only)
     uint32_t pw[8];         // P of the sub-tile awaiting its product half-step,
                             // packed bf16 pairs: pw[4u + i] = dword i of B operand u
     float m;                // running max (log2 domain), same in lanes i and i ^ 32
@@ -468,11 +478,21 @@ struct MfmaKernel {
 
   // Plain S of one sub-tile (the item's first).
   static __device__ __forceinline__ void s_tile(uint32_t kt, uint32_t rt, const QFrag* qf,
-                                                State& w) {
+                                                const bf16x8* qr, State& w) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) w.st[r] = 0.f;
+    if constexpr (C::MIXED) {
 #pragma unroll
-    for (int s = 0; s < C::S_STEPS; ++s) w.st = s_mfma(s_frag(kt, rt, s), qf[s], w.st);
+      for (int s = 0; s < C::QK_STEPS; ++s) w.st = s_mfma(s_frag(kt, rt, s), qf[s], w.st);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w.sr[r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < C::ROPE_STEPS; ++s) w.sr = r_mfma(r_frag(rt, s), qr[s], w.sr);
+    } else {
+      (void)qr;
+#pragma unroll
+      for (int s = 0; s < C::S_STEPS; ++s) w.st = s_mfma(s_frag(kt, rt, s), qf[s], w.st);
+    }
   }
 
   // Softmax half-step of a sub-tile whose S is in w.st: fp8 k_scale, the mask
@@ -481,16 +501,25 @@ struct MfmaKernel {
   // row sums and the bf16 packing of P into w.pw.  Element e of a lane is key
   // 8(e/4) + 4 hf + e%4 of the sub-tile.
   template <int OP0, int OP1, bool MAYMASK>
-  static __device__ __forceinline__ void xphase(State& w, const float* ks, int hf, float cq,
-                                                bool mask, int rel, const BlockDma& bd,
-                                                const DmaLanes& dl, uint32_t junk, int wave) {
+  static __device__ __forceinline__ void xphase(State& w, const float* ks, int hf, float cq_in,
+                                                float crope, bool mask, int rel,
+                                                const BlockDma& bd, const DmaLanes& dl,
+                                                uint32_t junk, int wave) {
     MHA_SLOT_FENCE();
     // this half-step's share of the block's DMA ops
     dma_ops<OP0, OP1>(bd, dl, junk, wave);
     float x = -INFINITY;
+    // mixed layout: the score goes straight to the log2 domain here
+    // (q_scale k_scale S_nope and S_rope at their own multipliers); the
+    // rest of the half-step then runs with multiplier 1
+    const float cq = C::MIXED ? 1.f : cq_in;
+    (void)crope;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      if constexpr (C::FP8) w.st[e] *= ks[8 * (e >> 2) + 4 * hf + (e & 3)];
+      if constexpr (C::MIXED)
+        w.st[e] = fmaf(w.st[e] * ks[8 * (e >> 2) + 4 * hf + (e & 3)], cq_in, w.sr[e] * crope);
+      else if constexpr (C::FP8)
+        w.st[e] *= ks[8 * (e >> 2) + 4 * hf + (e & 3)];
       x = fmaxf(x, w.st[e]);
     }
     if (MAYMASK && mask) {
@@ -533,7 +562,7 @@ struct MfmaKernel {
   template <int KH, int VH>
   static __device__ __forceinline__ void gphase(State& w, uint32_t kb, uint32_t rb,
                                                 const uint32_t (&vb)[C::DV_TILES],
-                                                const QFrag* qf) {
+                                                const QFrag* qf, const bf16x8* qr) {
     // K rows of half KH of the K block, V rows of half VH of the V block
     const uint32_t kn = kb + KH * 32 * C::K_RP, rn = rb + KH * 32 * C::R_RP;
     uint32_t vh[C::DV_TILES];
@@ -546,9 +575,13 @@ struct MfmaKernel {
     for (int u = 0; u < 2; ++u)
       pb[u] = __builtin_bit_cast(bf16x8, i32x4{(int)w.pw[4 * u], (int)w.pw[4 * u + 1],
                                                (int)w.pw[4 * u + 2], (int)w.pw[4 * u + 3]});
-    f32x16 sn;
+    f32x16 sn, srn;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sn[r] = 0.f;
+    if constexpr (C::MIXED) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) srn[r] = 0.f;
+    }
     // products alternate between the P V and the S streams while both last
     static_for<0, NS>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
@@ -558,6 +591,8 @@ struct MfmaKernel {
       if constexpr (PV) {
         w.o[idx % C::DV_TILES] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             v_frag(vh, idx), pb[idx / C::DV_TILES], w.o[idx % C::DV_TILES], 0, 0, 0);
+      } else if constexpr (C::MIXED && idx >= C::QK_STEPS) {
+        srn = r_mfma(r_frag(rn, idx - C::QK_STEPS), qr[idx - C::QK_STEPS], srn);
       } else {
         sn = s_mfma(s_frag(kn, rn, idx), qf[idx], sn);
       }
@@ -571,11 +606,14 @@ struct MfmaKernel {
       constexpr int NPAIR = C::NPV < C::S_STEPS ? C::NPV : C::S_STEPS;
       if constexpr (k < NS) {
         constexpr bool PV = k < 2 * NPAIR ? (k % 2 == 0) : (C::NPV > C::S_STEPS);
-        __builtin_amdgcn_sched_group_barrier(0x100, PV ? 2 : (C::FP8 ? 2 : 1), 0);
+        constexpr int idx = k < 2 * NPAIR ? k / 2 : k - NPAIR;
+        __builtin_amdgcn_sched_group_barrier(0x100, PV ? 2 : (C::FP8 && idx < C::QK_STEPS ? 2 : 1),
+                                             0);
       }
       if constexpr (k >= RA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     });
     w.st = sn;
+    if constexpr (C::MIXED) w.sr = srn;
     MHA_SLOT_FENCE();
   }
 
@@ -650,9 +688,20 @@ struct MfmaKernel {
       // Q fragments (B operand): lane -> query qi, 8 (bf16) or 32 (fp8)
       // consecutive depth elements per step and lane half; rope steps follow
       // the nope steps.
-      QFrag qf[C::S_STEPS];
+      QFrag qf[C::MIXED ? C::QK_STEPS : C::S_STEPS];
+      bf16x8 qr[C::MIXED ? C::ROPE_STEPS : 1];  // mixed layout: the rope steps
 #pragma unroll
       for (int s = 0; s < C::S_STEPS; ++s) {
+        if constexpr (C::MIXED) {
+          if (s >= C::QK_STEPS) {
+            i32x4 x = {0, 0, 0, 0};
+            if (qvalid)
+              x = *reinterpret_cast<const i32x4*>(
+                  qrp + (qrow * C::DR + (s - C::QK_STEPS) * 16 + 8 * hf) * 2);
+            qr[s - C::QK_STEPS] = __builtin_bit_cast(bf16x8, x);
+            continue;
+          }
+        }
         if constexpr (C::FP8) {
           i32x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
           if (qvalid) {
@@ -707,7 +756,7 @@ struct MfmaKernel {
       __syncthreads();
       if (has_sub) {
         const uint32_t ks0 = sbase + (uint32_t)(jlo % C::NKS) * C::KSLOT;
-        s_tile(opaque(ks0 + C::K_OFF + ln.k), opaque(ks0 + C::R_OFF + ln.r), qf, w);
+        s_tile(opaque(ks0 + C::K_OFF + ln.k), opaque(ks0 + C::R_OFF + ln.r), qf, qr, w);
       }
       if constexpr (C::KLEAD == 3)
         if (grp == 0) dma_ops<0, C::N_OPS>(blk(jlo - 1), dl, junk, wave);
@@ -735,7 +784,7 @@ struct MfmaKernel {
         const float* ks =
             reinterpret_cast<const float*>(smem + (j % C::NKS) * C::KSLOT + C::KS_OFF) + 32 * H;
         if (!CHK || i < n_sub)
-          xphase<O0, O1, CHK>(w, ks, hf, cq, SPLIT ? i == last_sub : i == n_sub - 1,
+          xphase<O0, O1, CHK>(w, ks, hf, cq, p.scale_log2, SPLIT ? i == last_sub : i == n_sub - 1,
                               lim - 32 * i - 4 * hf, bd, dl, junk, wave);
         else
           dma_ops<O0, O1>(bd, dl, junk, wave);
@@ -751,7 +800,7 @@ struct MfmaKernel {
           for (int t = 0; t < C::DV_TILES; ++t) vb[t] = opaque(vs + ln.v[t]);
           gphase<decltype(kh)::value, decltype(vh_)::value>(
               w, opaque(ks + C::K_OFF + ln.k), C::DR > 0 ? opaque(ks + C::R_OFF + ln.r) : 0u, vb,
-              qf);
+              qf, qr);
         }
       };
       using P0 = std::integral_constant<int, 0>;

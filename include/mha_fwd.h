@@ -88,9 +88,11 @@ typedef enum {
  *   head_dim_nope, head_dim_rope, v_dim   Dn, Dr (0 = no rope part), Dv
  *   q_rope      [T, num_heads, head_dim_rope], k_rope [T, num_kv_heads,
  *               head_dim_rope]: the rope part of Q and K, already rotated,
- *               bfloat16 (float32 for F32).  NULL iff head_dim_rope == 0
- *               (SM100AttentionSMem, Parameters: rope_dtype_; Methods:
- *               q_rope_smem).
+ *               bfloat16 (float32 for F32; bfloat16 also under FP8_E4M3,
+ *               where q_scale / k_scale scale the nope product only:
+ *               S = sigma (q_scale k_scale q_nope . k_nope + q_rope . k_rope)).
+ *               NULL iff head_dim_rope == 0 (SM100AttentionSMem, Parameters:
+ *               rope_dtype_, its own element type; Methods: q_rope_smem).
  *   causal      0: every key of the sequence is visible; 1: key j visible to
  *               query i iff j <= i
  *   softmax_scale  sigma; <= 0 selects 1/sqrt(head_dim_nope + head_dim_rope)
@@ -104,7 +106,7 @@ typedef enum {
  * Compiled set (MHA_ERR_UNSUPPORTED otherwise):
  *   F32      (Dn, Dr, Dv) in {(64,0,64), (128,0,128), (128,64,128)}
  *   BF16     (Dn, Dr, Dv) in {(64,0,64), (128,0,128), (128,64,128)}
- *   FP8_E4M3 (Dn, Dr, Dv) in {(128,0,128)}
+ *   FP8_E4M3 (Dn, Dr, Dv) in {(128,0,128), (128,64,128)}
  *
  * The library owns a small workspace per (device, stream): the work table and
  * queue counters of the persistent scheduler.  It is allocated on the first

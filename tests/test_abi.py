@@ -71,7 +71,7 @@ def test_invalid_arguments_rejected(over):
                                   dict(dtype=nat.MHA_DTYPE_FP8_E4M3, q_scale=FAKE,
                                        k_scale=FAKE, dn=64, dv=64),
                                   dict(dtype=nat.MHA_DTYPE_FP8_E4M3, q_scale=FAKE,
-                                       k_scale=FAKE, dr=64, q_rope=FAKE, k_rope=FAKE)])
+                                       k_scale=FAKE, dr=32, q_rope=FAKE, k_rope=FAKE)])
 def test_unsupported_shapes(over):
     assert call(**over) == nat.MHA_ERR_UNSUPPORTED
 
@@ -86,7 +86,7 @@ def test_supported_set():
     want = {
         nat.MHA_DTYPE_F32: {(64, 0, 64), (128, 0, 128), (128, 64, 128)},
         nat.MHA_DTYPE_BF16: {(64, 0, 64), (128, 0, 128), (128, 64, 128)},
-        nat.MHA_DTYPE_FP8_E4M3: {(128, 0, 128)},
+        nat.MHA_DTYPE_FP8_E4M3: {(128, 0, 128), (128, 64, 128)},
     }
     for dt, shapes in want.items():
         for dn in (32, 64, 96, 128, 192, 256):

@@ -34,6 +34,8 @@ SMALL = [
     ("fp8", [300, 50], 4, 4, 128, 0, 128, False),
     ("fp8", [257], 8, 2, 128, 0, 128, True),
     ("fp8", [900], 2, 2, 128, 0, 128, True),
+    ("fp8", [333, 20], 4, 4, 128, 64, 128, True),
+    ("fp8", [650], 2, 1, 128, 64, 128, False),
     ("f32", [100, 3], 2, 2, 128, 0, 128, True),
     ("f32", [70], 2, 1, 128, 64, 128, True),
     ("f32", [130, 1], 2, 2, 64, 0, 64, True),
@@ -72,7 +74,7 @@ def test_fp32_dense_workload_full():
     print(f"fp32 workload: O err {eo:.3e}, LSE err {el:.3e}")
 
 
-@pytest.mark.parametrize("name", mi.WORKLOAD_ORDER[1:])
+@pytest.mark.parametrize("name", mi.WORKLOAD_ORDER[1:] + list(mi.EXTRA_WORKLOADS))
 def test_full_size_workloads_sampled(name):
     print("workload", name, flush=True)
     inp = mi.workload(name)
