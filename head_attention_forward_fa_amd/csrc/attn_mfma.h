@@ -543,11 +543,11 @@ struct MfmaKernel {
       w.m = m_new;
     }
     const float m_use = w.m == -INFINITY ? 0.f : w.m;
-    float ls[2] = {0.f, 0.f};
+    float ls[2];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       w.st[e] = fast_exp2(fmaf(w.st[e], cq, -m_use));
-      ls[e & 1] += w.st[e];
+      ls[e & 1] = e < 2 ? w.st[e] : ls[e & 1] + w.st[e];  // no add of the zero start
       if (e & 1) w.pw[e >> 1] = pack_bf16x2(w.st[e - 1], w.st[e]);
     }
     w.l += ls[0] + ls[1];
