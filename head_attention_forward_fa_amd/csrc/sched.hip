@@ -12,12 +12,16 @@
 //
 //   * a one-workgroup prepass turns cu_seqlens into a table of work items
 //     {s0, L, h, q-tile, b} (times the key splits under split-KV: one item
-//     per split, next to each other).  Items are grouped by (sequence, KV head), so
-//     that the query heads sharing a KV head and every q-tile of that
-//     sequence sit next to each other; groups are dealt to 8 queues, one per
-//     XCD, largest first in a snake order so the queues carry equal work;
-//     inside a group the q-tiles run longest first (causal cost grows with
-//     the tile index).
+//     per split, next to each other).  Groups are (sequence, KV head): the
+//     query heads sharing a KV head sit next to each other.  Groups are
+//     ranked by cost (bitonic sort in LDS) and dealt to 8 queues, one per
+//     XCD, largest first in a snake order so the queues carry equal work.
+//     A queue runs chunk by chunk (a chunk: consecutive groups), a chunk in
+//     rounds: round k holds the k-th longest q-tile of each of its groups
+//     (causal cost grows with the tile index).  Causal: one chunk per
+//     queue, so the queue drains with short items and the CUs finish close
+//     together.  Non-causal: one group per chunk (equal costs; a group's
+//     items share their K/V in the XCD's L2).
 //   * the attention kernel is launched with about (CUs x resident
 //     workgroups) workgroups; each pops items from queue blockIdx % 8 with
 //     one atomic add, then helps the other queues once its own is empty.
@@ -46,16 +50,21 @@ __device__ __forceinline__ int snake_bin(int r) {
   int p = r / kNumXcd, j = r % kNumXcd;
   return (p & 1) ? (kNumXcd - 1 - j) : j;
 }
+// rank of the group at position j of queue x under the snake deal
+__device__ __forceinline__ int queue_rank(int x, int j) {
+  return 2 * kNumXcd * (j >> 1) + ((j & 1) ? 2 * kNumXcd - 1 - x : x);
+}
 
 __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
     const int32_t* __restrict__ cu, int batch, int num_heads, int num_kv_heads, int causal,
-    int bm, int bn, int num_splits, int capacity, i32x4* __restrict__ table,
+    int bm, int bn, int num_splits, int capacity, int chunk, i32x4* __restrict__ table,
     SchedState* __restrict__ st, int* __restrict__ scratch) {
   __shared__ long long s_cost[kSortedMax];
   __shared__ int s_items[kSortedMax];   // group -> item count
   __shared__ int s_irank[kSortedMax];   // rank -> item count
   __shared__ int s_grank[kSortedMax];   // group -> rank
   __shared__ int s_off[kSortedMax];     // rank -> offset inside its queue
+  __shared__ int s_gidx[kSortedMax];    // rank -> group (after the sort)
   __shared__ int s_fill[kNumXcd];
   __shared__ int s_base[kNumXcd];
   __shared__ int s_bad;
@@ -104,17 +113,37 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
   }
 
   if (sorted) {
-    // B: rank groups by cost, largest first (ties by index)
-    for (int i = tid; i < n; i += kPrepassThreads) {
-      const long long c = s_cost[i];
-      int rank = 0;
-#pragma unroll 8
-      for (int j = 0; j < n; ++j) {
-        const long long cj = s_cost[j];
-        rank += (cj > c) || (cj == c && j < i);
+    // B: rank groups by cost, largest first (ties by index): bitonic sort
+    // of (cost, index) in LDS, padded to a power of two with cost -1
+    int np = 1;
+    while (np < n) np <<= 1;
+    for (int i = tid; i < np; i += kPrepassThreads) {
+      if (i >= n) s_cost[i] = -1;
+      s_gidx[i] = i;
+    }
+    __syncthreads();
+    for (int k = 2; k <= np; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int t = tid; t < np; t += kPrepassThreads) {
+          const int u = t ^ j;
+          if (u > t) {
+            const long long ct = s_cost[t], cu2 = s_cost[u];
+            const int it = s_gidx[t], iu = s_gidx[u];
+            const bool t_first = ct > cu2 || (ct == cu2 && it < iu);
+            if (((t & k) == 0) != t_first) {  // (t & k) == 0: this run goes in final order
+              s_cost[t] = cu2;
+              s_cost[u] = ct;
+              s_gidx[t] = iu;
+              s_gidx[u] = it;
+            }
+          }
+        }
+        __syncthreads();
       }
-      s_grank[i] = rank;
-      s_irank[rank] = s_items[i];
+    for (int r = tid; r < n; r += kPrepassThreads) {
+      const int i = s_gidx[r];
+      s_grank[i] = r;
+      s_irank[r] = s_items[i];
     }
     __syncthreads();
     // C: snake-deal ranks to queues (rank r -> queue snake_bin(r)); queue x
@@ -184,24 +213,60 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
   }
   __syncthreads();
 
-  // E: write the items of each group, q-tiles longest first, heads inner
+  // E: write the items of each group: per q-tile, its query heads (and
+  // their key splits) next to each other.  Sorted path: a queue is cut into
+  // chunks of `chunk` consecutive groups; a chunk runs in rounds, round k
+  // holding the k-th longest q-tile of each of its groups that has one, in
+  // queue order.  The queue's groups come in non-increasing q-tile count
+  // (cost order implies it), so round k is the chunk's first C_k groups,
+  // and the rounds before it hold sum_j min(nqt_j, k) q-tiles.  Unsorted
+  // path: each group's q-tiles back to back, longest first.
+  const int u = group * num_splits;  // items per (group, q-tile)
+  const int qlen = 2 * ((n + 2 * kNumXcd - 1) / (2 * kNumXcd));  // queue positions, upper bound
   for (int i = tid; i < n; i += kPrepassThreads) {
     const int b = i / num_kv_heads;
     const int g = i % num_kv_heads;
     const int s0 = cu[b];
     const int L = cu[b + 1] - s0;
     const int nqt = L > 0 ? (L + bm - 1) / bm : 0;
-    int pos;
-    if (sorted) {
-      const int r = s_grank[i];
-      pos = s_base[snake_bin(r)] + s_off[r];
-    } else {
-      pos = scratch[i];  // queues are contiguous in index order
-    }
-    for (int qt = nqt - 1; qt >= 0; --qt)
+    for (int k = 0; k < nqt; ++k) {
+      const int qt = nqt - 1 - k;
+      long long pos;
+      if (sorted) {
+        const int r = s_grank[i];
+        const int x = snake_bin(r);
+        const int jq = 2 * (r / (2 * kNumXcd)) + (r % (2 * kNumXcd) < kNumXcd ? 0 : 1);
+        // the chunk [c0, c1) of queue positions holding this group
+        const int c0 = jq - jq % chunk;
+        const int c1 = min(c0 + chunk, qlen);
+        // items at queue positions < j (positions past the queue's end map
+        // to ranks >= n)
+        auto prefix = [&](int j) -> long long {
+          const int rr = queue_rank(x, j);
+          return rr < n ? s_off[rr] : s_fill[x];
+        };
+        // C_k: the first chunk position whose group has at most k q-tiles
+        const long long lim = (long long)k * u;
+        int lo = c0, hi = c1;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          const int rm = queue_rank(x, mid);
+          const long long a = rm < n ? s_irank[rm] : 0;
+          if (a > lim)
+            lo = mid + 1;
+          else
+            hi = mid;
+        }
+        pos = s_base[x] + prefix(c0) + lim * (lo - c0) + (prefix(c1) - prefix(lo)) +
+              (long long)(jq - c0) * u;
+      } else {
+        pos = scratch[i] + (long long)k * u;  // queues are contiguous in index order
+      }
       for (int hh = 0; hh < group; ++hh)
-        for (int sp = 0; sp < num_splits; ++sp)
-          table[pos++] = i32x4{s0, L, ((g * group + hh) << 20) | qt, (sp << 24) | b};
+        for (int sp = 0; sp < num_splits; ++sp, ++pos)
+          if (pos < total)
+            table[pos] = i32x4{s0, L, ((g * group + hh) << 20) | qt, (sp << 24) | b};
+    }
   }
 }
 
@@ -236,11 +301,12 @@ __global__ __launch_bounds__(256) void sched_visit_kernel(int batch, int num_hea
 }  // namespace
 
 hipError_t launch_prepass(const int32_t* cu, int batch, int num_heads, int num_kv_heads,
-                          int causal, int bm, int bn, int num_splits, int capacity,
+                          int causal, int bm, int bn, int num_splits, int capacity, int chunk,
                           i32x4* table, SchedState* st, int* scratch, hipStream_t stream) {
+  if (chunk < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(sched_prepass_kernel, dim3(1), dim3(kPrepassThreads), 0, stream, cu, batch,
-                     num_heads, num_kv_heads, causal, bm, bn, num_splits, capacity, table, st,
-                     scratch);
+                     num_heads, num_kv_heads, causal, bm, bn, num_splits, capacity, chunk, table,
+                     st, scratch);
   return hipGetLastError();
 }
 

@@ -194,3 +194,26 @@ def test_scheduler_many_groups_index_mode():
     for b, L in enumerate(lens):
         want[:, b, : (L + 255) // 256] = 1
     assert np.array_equal(visits.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("nseq,hkv,maxlen", [(511, 4, 2600), (256, 8, 2600), (9, 1, 2600),
+                                            (300, 2, 600)])
+def test_scheduler_ranked_groups_cover_every_item_once(nseq, hkv, maxlen, causal):
+    # groups ranked in LDS (up to 2048 of them, padded to a power of two for
+    # the sort) and laid out chunk by chunk, round by round, in each queue
+    # (short sequences: chunks of many groups)
+    from head_attention_forward_fa_amd import mha_sched_visit
+    rng = np.random.default_rng(nseq)
+    lens = rng.integers(0, maxlen, size=nseq)
+    lens[0] = 0
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    hq = 2 * hkv
+    mx = int(lens.max())
+    visits = mha_sched_visit(torch.from_numpy(cu).cuda(), mx, hq, hkv, causal, 256, 0)
+    torch.cuda.synchronize()
+    tiles = (mx + 255) // 256
+    want = np.zeros((hq, len(lens), tiles), dtype=np.int32)
+    for b, L in enumerate(lens):
+        want[:, b, : (L + 255) // 256] = 1
+    assert np.array_equal(visits.cpu().numpy(), want)
