@@ -37,6 +37,7 @@ namespace {
 
 constexpr int kPrepassThreads = 1024;
 constexpr int kSortedMax = 2048;  // groups ranked in LDS up to this count
+constexpr int kRankDirect = 384;  // up to this many: rank by counting (else sort)
 
 __device__ __forceinline__ long long group_cost(int L, int bm, int bn, int causal) {
   if (L <= 0) return 0;
@@ -79,6 +80,7 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
   // A: per-group cost and item count; the item total by a block reduction
   // (in 64 bits: garbage lengths must not wrap past the capacity check)
   long long my_items = 0;
+  int my_rmax = 0;  // most q-tiles of a group
   for (int i = tid; i < n; i += kPrepassThreads) {
     const int b = i / num_kv_heads;
     const int L = cu[b + 1] - cu[b];
@@ -86,6 +88,7 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
     if (L < 0 || nqt >= kMaxQTilesPerSeq) s_bad = 1;
     const int items = nqt * group * num_splits;
     my_items += items;
+    my_rmax = max(my_rmax, nqt);
     if (sorted) {
       s_cost[i] = group_cost(L, bm, bn, causal) * group;
       s_items[i] = items;
@@ -93,12 +96,23 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
       scratch[i] = items;
     }
   }
-  for (int d = kWave / 2; d > 0; d >>= 1) my_items += __shfl_down(my_items, d);
+  for (int d = kWave / 2; d > 0; d >>= 1) {
+    my_items += __shfl_down(my_items, d);
+    my_rmax = max(my_rmax, __shfl_down(my_rmax, d));
+  }
   __shared__ long long s_wsum[kPrepassThreads / kWave];
-  if ((tid & (kWave - 1)) == 0) s_wsum[tid / kWave] = my_items;
+  __shared__ int s_wmax[kPrepassThreads / kWave];
+  if ((tid & (kWave - 1)) == 0) {
+    s_wsum[tid / kWave] = my_items;
+    s_wmax[tid / kWave] = my_rmax;
+  }
   __syncthreads();
   long long total = 0;
-  for (int w = 0; w < kPrepassThreads / kWave; ++w) total += s_wsum[w];
+  int rmax = 0;
+  for (int w = 0; w < kPrepassThreads / kWave; ++w) {
+    total += s_wsum[w];
+    rmax = max(rmax, s_wmax[w]);
+  }
   if (s_bad || total > (long long)capacity) {
     if (tid < kNumXcd) {
       st->q[tid].counter = 0;
@@ -113,8 +127,17 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
   }
 
   if (sorted) {
-    // B: rank groups by cost, largest first (ties by index): bitonic sort
-    // of (cost, index) in LDS, padded to a power of two with cost -1
+    // B: rank groups by cost, largest first (ties by index).  Equal costs
+    // (a uniform batch): the index order.  Up to kRankDirect groups: each
+    // group counts the groups ahead of it.  More: bitonic sort of (cost,
+    // index) in LDS, padded to a power of two with cost -1.
+    __shared__ int s_uniform;
+    if (tid == 0) s_uniform = 1;
+    __syncthreads();
+    for (int i = tid + 1; i < n; i += kPrepassThreads)
+      if (s_cost[i] != s_cost[0]) s_uniform = 0;
+    __syncthreads();
+    const bool direct = s_uniform || n <= kRankDirect;
     int np = 1;
     while (np < n) np <<= 1;
     for (int i = tid; i < np; i += kPrepassThreads) {
@@ -122,7 +145,20 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
       s_gidx[i] = i;
     }
     __syncthreads();
-    for (int k = 2; k <= np; k <<= 1)
+    if (direct && !s_uniform) {
+      for (int i = tid; i < n; i += kPrepassThreads) {
+        const long long c = s_cost[i];
+        int rank = 0;
+#pragma unroll 8
+        for (int j = 0; j < n; ++j) {
+          const long long cj = s_cost[j];
+          rank += (cj > c) || (cj == c && j < i);
+        }
+        s_gidx[rank] = i;
+      }
+      __syncthreads();
+    }
+    for (int k = 2; k <= (direct ? 1 : np); k <<= 1)
       for (int j = k >> 1; j > 0; j >>= 1) {
         for (int t = tid; t < np; t += kPrepassThreads) {
           const int u = t ^ j;
@@ -221,52 +257,57 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
   // (cost order implies it), so round k is the chunk's first C_k groups,
   // and the rounds before it hold sum_j min(nqt_j, k) q-tiles.  Unsorted
   // path: each group's q-tiles back to back, longest first.
+  // One (group, round) pair per thread and step: a group's rounds spread
+  // over the threads.
   const int u = group * num_splits;  // items per (group, q-tile)
   const int qlen = 2 * ((n + 2 * kNumXcd - 1) / (2 * kNumXcd));  // queue positions, upper bound
-  for (int i = tid; i < n; i += kPrepassThreads) {
+  const long long npairs = (long long)n * rmax;
+  for (long long t = tid; t < npairs; t += kPrepassThreads) {
+    const int i = (int)(t / rmax);
+    const int k = (int)(t % rmax);
     const int b = i / num_kv_heads;
     const int g = i % num_kv_heads;
     const int s0 = cu[b];
     const int L = cu[b + 1] - s0;
     const int nqt = L > 0 ? (L + bm - 1) / bm : 0;
-    for (int k = 0; k < nqt; ++k) {
-      const int qt = nqt - 1 - k;
-      long long pos;
-      if (sorted) {
-        const int r = s_grank[i];
-        const int x = snake_bin(r);
-        const int jq = 2 * (r / (2 * kNumXcd)) + (r % (2 * kNumXcd) < kNumXcd ? 0 : 1);
-        // the chunk [c0, c1) of queue positions holding this group
-        const int c0 = jq - jq % chunk;
-        const int c1 = min(c0 + chunk, qlen);
-        // items at queue positions < j (positions past the queue's end map
-        // to ranks >= n)
-        auto prefix = [&](int j) -> long long {
-          const int rr = queue_rank(x, j);
-          return rr < n ? s_off[rr] : s_fill[x];
-        };
-        // C_k: the first chunk position whose group has at most k q-tiles
-        const long long lim = (long long)k * u;
-        int lo = c0, hi = c1;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          const int rm = queue_rank(x, mid);
-          const long long a = rm < n ? s_irank[rm] : 0;
-          if (a > lim)
-            lo = mid + 1;
-          else
-            hi = mid;
-        }
-        pos = s_base[x] + prefix(c0) + lim * (lo - c0) + (prefix(c1) - prefix(lo)) +
-              (long long)(jq - c0) * u;
-      } else {
-        pos = scratch[i] + (long long)k * u;  // queues are contiguous in index order
+    if (k >= nqt) continue;
+    const int qt = nqt - 1 - k;
+    long long pos;
+    if (sorted) {
+      const int r = s_grank[i];
+      const int x = snake_bin(r);
+      const int jq = 2 * (r / (2 * kNumXcd)) + (r % (2 * kNumXcd) < kNumXcd ? 0 : 1);
+      // the chunk [c0, c1) of queue positions holding this group
+      const int c0 = jq - jq % chunk;
+      const int c1 = min(c0 + chunk, qlen);
+      // items at queue positions < j (positions past the queue's end map to
+      // ranks >= n)
+      auto prefix = [&](int j) -> long long {
+        const int rr = queue_rank(x, j);
+        return rr < n ? s_off[rr] : s_fill[x];
+      };
+      // C_k: the first chunk position whose group has at most k q-tiles
+      // (none before this group's position: those have at least as many)
+      const long long lim = (long long)k * u;
+      int lo = jq + 1, hi = c1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const int rm = queue_rank(x, mid);
+        const long long a = rm < n ? s_irank[rm] : 0;
+        if (a > lim)
+          lo = mid + 1;
+        else
+          hi = mid;
       }
-      for (int hh = 0; hh < group; ++hh)
-        for (int sp = 0; sp < num_splits; ++sp, ++pos)
-          if (pos < total)
-            table[pos] = i32x4{s0, L, ((g * group + hh) << 20) | qt, (sp << 24) | b};
+      pos = s_base[x] + prefix(c0) + lim * (lo - c0) + (prefix(c1) - prefix(lo)) +
+            (long long)(jq - c0) * u;
+    } else {
+      pos = scratch[i] + (long long)k * u;  // queues are contiguous in index order
     }
+    for (int hh = 0; hh < group; ++hh)
+      for (int sp = 0; sp < num_splits; ++sp, ++pos)
+        if (pos < total)
+          table[pos] = i32x4{s0, L, ((g * group + hh) << 20) | qt, (sp << 24) | b};
   }
 }
 
