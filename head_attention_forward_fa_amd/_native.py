@@ -23,7 +23,7 @@ MHA_ERR_HIP = 3
 
 EXPORTS = ("mha_fwd", "mha_fwd_last_error", "mha_fwd_supported", "mha_fwd_kernel_info",
            "mha_fwd_set_kernel_events", "mha_sched_visit", "mha_quantize_fp8",
-           "mha_fwd_splitkv", "mha_combine_splits")
+           "mha_fwd_splitkv", "mha_combine_splits", "mha_fwd_auto_splits")
 
 _lib = None
 
@@ -77,6 +77,8 @@ def load() -> ctypes.CDLL:
     lib.mha_fwd_splitkv.restype = ctypes.c_int
     lib.mha_combine_splits.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.mha_combine_splits.restype = ctypes.c_int
+    lib.mha_fwd_auto_splits.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.mha_fwd_auto_splits.restype = ctypes.c_int
     _lib = lib
     return lib
 

@@ -3,6 +3,7 @@
 // kernel variants.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <map>
@@ -133,11 +134,46 @@ int check_scalars(int32_t batch, int32_t max_seqlen, int32_t num_heads,
   return MHA_OK;
 }
 
+// Key splits for mha_fwd.  With every sequence taken at max_seqlen (an upper
+// bound the host can compute without reading cu_seqlens), the run lasts at
+// least as long as the longest item (nb blocks) and as the average work per
+// CU; when the longest item exceeds that average by more than a quarter, its
+// keys are split so that a split is about half the average (the scheduler
+// then has pieces to even the CUs out with), with at least 8 blocks per
+// split, at most 8 splits, and at most 1 GiB of partials.
+int auto_splits(long long batch, long long max_seqlen, long long num_heads, int causal,
+                long long v_dim, int bm, int bn, int cus) {
+  if (batch < 1 || max_seqlen < 1 || num_heads < 1 || cus < 1) return 1;
+  const long long tiles = (max_seqlen + bm - 1) / bm;
+  const long long nb = (max_seqlen + bn - 1) / bn;
+  long long per_tile_sum = 0;  // blocks of one (sequence, head)'s q-tiles
+  if (causal) {
+    const long long full = std::min(tiles, nb * bn / bm);  // tiles whose keys do not reach past the end
+    per_tile_sum = (bm / bn) * full * (full + 1) / 2 + (tiles - full) * nb;
+  } else {
+    per_tile_sum = tiles * nb;
+  }
+  const long long total = batch * num_heads * per_tile_sum;
+  const long long per_cu = (total + cus - 1) / cus;
+  if (4 * nb <= 5 * per_cu) return 1;
+  long long sp = (2 * nb + per_cu - 1) / std::max(1LL, per_cu);
+  sp = std::min({sp, 8LL, nb / 8});
+  const long long tokens = batch * max_seqlen;
+  while (sp > 1 && (sp * tokens * num_heads * v_dim * 4 > (1LL << 30) || tokens > INT_MAX / 2)) --sp;
+  return sp > 1 ? (int)sp : 1;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* mha_fwd_last_error(void) { return g_err.c_str(); }
+
+int mha_fwd_auto_splits(int32_t batch, int32_t max_seqlen, int32_t num_heads, int32_t causal,
+                        int32_t v_dim, int32_t cus) {
+  return auto_splits(batch, max_seqlen, num_heads, causal, v_dim, mha::kBlockM_Mfma,
+                     mha::kBlockN_Mfma, cus);
+}
 
 int mha_fwd_supported(int32_t dtype, int32_t head_dim_nope, int32_t head_dim_rope,
                       int32_t v_dim) {
@@ -182,19 +218,42 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   if (fp8 != (q_scale != nullptr) || fp8 != (k_scale != nullptr))
     return fail(MHA_ERR_INVALID_ARG, "q_scale and k_scale must be given iff dtype is FP8_E4M3");
 
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  // mha_fwd: key splits of its own where the longest items would set the
+  // run time, partials in the workspace (laid out for batch x max_seqlen
+  // tokens; the merge stops at the real total, cu_seqlens[batch])
+  const bool auto_split = num_splits == 1 && o_part == nullptr && var->launch_split != nullptr;
+  size_t part_bytes = 0;
+  if (auto_split) {
+    const int sp = auto_splits(batch, max_seqlen, num_heads, causal, v_dim, var->block_m,
+                               var->block_n, cu_count(dev));
+    if (sp > 1) {
+      num_splits = sp;
+      total_tokens = (int32_t)((long long)batch * max_seqlen);  // auto_splits keeps this within int
+      part_bytes = align_up((size_t)sp * total_tokens * num_heads * v_dim * sizeof(float), 256) +
+                   align_up((size_t)sp * num_heads * total_tokens * sizeof(float), 256);
+    }
+  }
+  const bool split_here = auto_split && num_splits > 1;
+
   Plan plan;
   rc = make_plan(batch, max_seqlen, num_heads, num_kv_heads, var->block_m, num_splits, &plan);
   if (rc) return rc;
 
   const float sigma =
       softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)(head_dim_nope + head_dim_rope));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
   char* ws = nullptr;
-  e = get_workspace(dev, s, plan.bytes, &ws);
+  e = get_workspace(dev, s, plan.bytes + part_bytes, &ws);
   if (e != hipSuccess) return fail_hip(e, "workspace allocation");
+  if (split_here) {
+    o_part = reinterpret_cast<float*>(ws + plan.bytes);
+    lse_part = reinterpret_cast<float*>(
+        ws + plan.bytes +
+        align_up((size_t)num_splits * total_tokens * num_heads * v_dim * sizeof(float), 256));
+  }
   auto* st = reinterpret_cast<mha::SchedState*>(ws);
   auto* table = reinterpret_cast<mha::i32x4*>(ws + kStateBytes);
   auto* scratch = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
@@ -242,7 +301,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
     if (e != hipSuccess) return fail_hip(e, "hipEventRecord (stop)");
   }
   if (num_splits > 1) {
-    e = mha::launch_combine(o_part, lse_part, num_splits, total_tokens, num_heads, v_dim,
+    e = mha::launch_combine(o_part, lse_part, num_splits, total_tokens,
+                            split_here ? cu_seqlens + batch : nullptr, num_heads, v_dim,
                             dtype != MHA_DTYPE_F32, o, lse, s);
     if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
   }
@@ -305,8 +365,8 @@ int mha_combine_splits(const float* o_partial, const float* lse_partial, int32_t
     return fail(MHA_ERR_INVALID_ARG, "o_partial, lse_partial, o, lse must be non-NULL");
   if (reinterpret_cast<uintptr_t>(o_partial) % 16 != 0 || reinterpret_cast<uintptr_t>(o) % 16 != 0)
     return fail(MHA_ERR_INVALID_ARG, "o_partial and o must be 16-byte aligned");
-  hipError_t e = mha::launch_combine(o_partial, lse_partial, num_splits, total_tokens, num_heads,
-                                     v_dim, out_dtype == MHA_DTYPE_BF16, o, lse,
+  hipError_t e = mha::launch_combine(o_partial, lse_partial, num_splits, total_tokens, nullptr,
+                                     num_heads, v_dim, out_dtype == MHA_DTYPE_BF16, o, lse,
                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
   return MHA_OK;

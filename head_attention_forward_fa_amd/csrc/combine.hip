@@ -28,16 +28,20 @@ namespace {
 
 constexpr int kCombineThreads = 256;
 
+// T: tokens of the partials' layout; t_out (device, may be null): tokens of
+// the output when fewer (the rest of the partial rows are not merged), else T
 template <int DV, bool BF16>
 __global__ __launch_bounds__(kCombineThreads) void combine_splits_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part, int num_splits, int T,
-    int H, void* __restrict__ o, float* __restrict__ lse) {
+    const int32_t* __restrict__ t_out, int H, void* __restrict__ o, float* __restrict__ lse) {
   constexpr int LPR = DV / 4;  // lanes per row
   constexpr int RPB = kCombineThreads / LPR;
   const int c = threadIdx.x % LPR;
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;  // row = t * H + h
   if (row >= (long long)T * H) return;
   const int t = (int)(row / H), h = (int)(row % H);
+  const int Tn = t_out ? min(*t_out, T) : T;
+  if (t >= Tn) return;
   const size_t split_stride_o = (size_t)T * H * DV;
   const size_t split_stride_l = (size_t)H * T;
   const float* lp = lse_part + (size_t)h * T + t;
@@ -66,32 +70,34 @@ __global__ __launch_bounds__(kCombineThreads) void combine_splits_kernel(
   } else {
     *reinterpret_cast<f32x4*>(static_cast<float*>(o) + (size_t)row * DV + 4 * c) = acc;
   }
-  if (c == 0) lse[(size_t)h * T + t] = total > 0.f ? m + __logf(total) : -INFINITY;
+  if (c == 0) lse[(size_t)h * Tn + t] = total > 0.f ? m + __logf(total) : -INFINITY;
 }
 
 template <int DV, bool BF16>
-hipError_t launch_dv(const float* o_part, const float* lse_part, int num_splits, int T, int H,
-                     void* o, float* lse, hipStream_t stream) {
+hipError_t launch_dv(const float* o_part, const float* lse_part, int num_splits, int T,
+                     const int32_t* t_out, int H, void* o, float* lse, hipStream_t stream) {
   constexpr int RPB = kCombineThreads / (DV / 4);
   const long long rows = (long long)T * H;
   const long long blocks = (rows + RPB - 1) / RPB;
   hipLaunchKernelGGL((combine_splits_kernel<DV, BF16>), dim3((unsigned)blocks),
-                     dim3(kCombineThreads), 0, stream, o_part, lse_part, num_splits, T, H, o,
-                     lse);
+                     dim3(kCombineThreads), 0, stream, o_part, lse_part, num_splits, T, t_out, H,
+                     o, lse);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, int num_splits, int T,
-                          int H, int dv, bool bf16_out, void* o, float* lse,
+                          const int32_t* t_out, int H, int dv, bool bf16_out, void* o, float* lse,
                           hipStream_t stream) {
   if (dv == 64)
-    return bf16_out ? launch_dv<64, true>(o_part, lse_part, num_splits, T, H, o, lse, stream)
-                    : launch_dv<64, false>(o_part, lse_part, num_splits, T, H, o, lse, stream);
+    return bf16_out ? launch_dv<64, true>(o_part, lse_part, num_splits, T, t_out, H, o, lse, stream)
+                    : launch_dv<64, false>(o_part, lse_part, num_splits, T, t_out, H, o, lse,
+                                           stream);
   if (dv == 128)
-    return bf16_out ? launch_dv<128, true>(o_part, lse_part, num_splits, T, H, o, lse, stream)
-                    : launch_dv<128, false>(o_part, lse_part, num_splits, T, H, o, lse, stream);
+    return bf16_out
+               ? launch_dv<128, true>(o_part, lse_part, num_splits, T, t_out, H, o, lse, stream)
+               : launch_dv<128, false>(o_part, lse_part, num_splits, T, t_out, H, o, lse, stream);
   return hipErrorInvalidValue;
 }
 

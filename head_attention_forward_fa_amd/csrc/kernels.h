@@ -39,7 +39,7 @@ hipError_t launch_fp8_quant(const void* x, bool bf16, int64_t rows, int cols, ui
 // Split-KV merge (combine.hip): o_part [num_splits, T, H, Dv] float32 and
 // lse_part [num_splits, H, T] -> o [T, H, Dv] (bf16 or float32), lse [H, T].
 hipError_t launch_combine(const float* o_part, const float* lse_part, int num_splits, int T,
-                          int H, int dv, bool bf16_out, void* o, float* lse,
+                          const int32_t* t_out, int H, int dv, bool bf16_out, void* o, float* lse,
                           hipStream_t stream);
 
 // A kernel variant: its launcher and its occupancy (resident workgroups per

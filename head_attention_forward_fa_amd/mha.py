@@ -228,3 +228,11 @@ def mha_combine_splits(o_partial: torch.Tensor, lse_partial: torch.Tensor, *,
                                            int(H), int(Dv), code, _ptr(o), _ptr(lse_t), stream)
     nat.check(st)
     return o, lse_t
+
+
+def mha_fwd_auto_splits(batch: int, max_seqlen: int, num_heads: int, causal: bool, v_dim: int,
+                        cus: int) -> int:
+    """Key splits mha_fwd chooses for a bf16 / fp8 problem on `cus` compute
+    units (host arithmetic, no device call)."""
+    return int(nat.load().mha_fwd_auto_splits(int(batch), int(max_seqlen), int(num_heads),
+                                              int(bool(causal)), int(v_dim), int(cus)))

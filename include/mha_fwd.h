@@ -108,12 +108,21 @@ typedef enum {
  *   BF16     (Dn, Dr, Dv) in {(64,0,64), (128,0,128), (128,64,128)}
  *   FP8_E4M3 (Dn, Dr, Dv) in {(128,0,128), (128,64,128)}
  *
- * The library owns a small workspace per (device, stream): the work table and
- * queue counters of the persistent scheduler.  It is allocated on the first
- * call for that pair (so the first call must not be inside a HIP graph
- * capture) and grown when a larger problem arrives.  Calls on one stream are
- * ordered and may follow each other freely; calls on two streams use two
- * workspaces.
+ * Key splits of its own (BF16 and FP8_E4M3): where the longest work items
+ * would set the run time (few, long items for the device's CUs, e.g. one
+ * long causal sequence with few heads), mha_fwd runs them as
+ * mha_fwd_splitkv would, with mha_fwd_auto_splits(batch, max_seqlen,
+ * num_heads, causal, v_dim, CUs) key ranges, the float32 partials in its
+ * workspace, and merges them; O and LSE agree with the unsplit run up to
+ * float32 rounding of the merge.  Never with fewer than 16 key blocks
+ * (max_seqlen <= 960).
+ *
+ * The library owns a workspace per (device, stream): the work table and
+ * queue counters of the persistent scheduler, and the partials of its own
+ * key splits.  It is allocated on the first call for that pair (so the first
+ * call must not be inside a HIP graph capture) and grown when a larger
+ * problem arrives.  Calls on one stream are ordered and may follow each other
+ * freely; calls on two streams use two workspaces.
  */
 int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
             const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
@@ -238,6 +247,22 @@ int mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float*
 int mha_combine_splits(const float* o_partial, const float* lse_partial, int32_t num_splits,
                        int32_t total_tokens, int32_t num_heads, int32_t v_dim, int32_t out_dtype,
                        void* o, float* lse, void* stream);
+
+/*
+ * mha_fwd_auto_splits -- the number of key splits mha_fwd chooses for a
+ * bf16 / fp8 problem (host arithmetic only, no device call).  With every
+ * sequence taken at max_seqlen, nb = ceil(max_seqlen / 64) key blocks for
+ * the longest work item and W = the blocks of all items (causal: q-tile t of
+ * 256 rows sees min(nb, 4 (t + 1)) blocks) over `cus` compute units: 1 when
+ * 4 nb <= 5 ceil(W / cus), else ceil(2 nb / ceil(W / cus)) capped at 8 and at
+ * nb / 8 (at least 8 blocks per split), lowered until the float32 partials
+ * (splits x batch x max_seqlen x num_heads x v_dim x 4 bytes) fit in 1 GiB.
+ * The split (SM100AttentionSMem, comptime members: MiscMBarsType takes the
+ * config's splitk_partitions) is the pages'; this rule for choosing it is
+ * the library's.  Returns >= 1; 1 for non-positive arguments.
+ */
+int mha_fwd_auto_splits(int32_t batch, int32_t max_seqlen, int32_t num_heads, int32_t causal,
+                        int32_t v_dim, int32_t cus);
 
 /*
  * mha_quantize_fp8 -- per-token fp8 quantisation of Q or K rows, the step in

@@ -142,3 +142,23 @@ def test_quantize_fp8_validation(over):
 def test_quantize_fp8_zero_rows_is_a_no_op():
     lib = nat.load()
     assert lib.mha_quantize_fp8(None, nat.MHA_DTYPE_F32, 0, 64, None, None, None) == nat.MHA_OK
+
+
+def test_auto_splits_rule():
+    from head_attention_forward_fa_amd import mha_fwd_auto_splits as auto
+    cus = 256
+    assert auto(4, 4096, 32, True, 128, cus) == 1        # many items: no split
+    assert auto(2, 8192, 16, True, 128, cus) == 1
+    assert auto(1, 16384, 4, False, 128, cus) == 1       # one full-length item per CU
+    # one causal sequence, 4 heads: 256 items, the longest 256 blocks against
+    # 130 blocks of work per CU: splits of about half of that
+    assert auto(1, 16384, 4, True, 128, cus) == 4
+    assert auto(1, 2048, 2, True, 128, cus) == 4         # capped at 8 blocks per split
+    assert auto(1, 960, 2, True, 128, cus) == 1          # fewer than 16 key blocks
+    assert auto(1, 1024, 2, True, 128, cus) == 2
+    assert auto(1, 1 << 20, 1, True, 128, 4096) <= 8     # capped at 8 splits
+    # 1 GiB of float32 partials at most: 2 x 2^20 tokens x 64 heads x 128 x 4 B > 1 GiB
+    assert auto(2, 1 << 20, 64, False, 128, 1 << 20) == 1
+    for bad in [(0, 100, 1), (1, 0, 1), (1, 100, 0)]:
+        assert auto(*bad, True, 128, cus) == 1
+    assert auto(1, 2048, 2, True, 128, 0) == 1
