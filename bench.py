@@ -238,23 +238,23 @@ def summarize_profile(prof: str, workload: str) -> str:
         f"# {KERNEL} on {workload}",
         "",
         "rocprofv3 on one MI355X (gfx950), launched from the repository root after",
-        "`cd /tmp && export TMPDIR=/tmp`; R is the repository root:",
+        "`cd /tmp && export TMPDIR=/tmp`; P is the profile output directory:",
         "",
         "```",
-        f"rocprofv3 --kernel-trace --stats -f csv -T -d gpurun_out/prof/trace -o run -- {bench_cmd}",
+        f"rocprofv3 --kernel-trace --stats -f csv -T -d $P/trace -o run -- {bench_cmd}",
         f"rocprofv3 --pmc SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
         f"SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_LDS GRBM_GUI_ACTIVE -f csv -T "
-        f"-d gpurun_out/prof/pmcA -o run -- {bench_cmd}",
+        f"-d $P/pmcA -o run -- {bench_cmd}",
         f"rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAIT_ANY "
         f"SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_LDS SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE "
-        f"-f csv -T -d gpurun_out/prof/pmcB -o run -- {bench_cmd}",
-        f"rocprofv3 --pmc FETCH_SIZE -f csv -T -d gpurun_out/prof/pmcC -o run -- {bench_cmd}",
-        f"rocprofv3 --pmc WRITE_SIZE -f csv -T -d gpurun_out/prof/pmcD -o run -- {bench_cmd}",
-        f"rocprofv3 --pmc FETCH_SIZE -f csv -T -d gpurun_out/prof/copy_fetch -o run -- "
+        f"-f csv -T -d $P/pmcB -o run -- {bench_cmd}",
+        f"rocprofv3 --pmc FETCH_SIZE -f csv -T -d $P/pmcC -o run -- {bench_cmd}",
+        f"rocprofv3 --pmc WRITE_SIZE -f csv -T -d $P/pmcD -o run -- {bench_cmd}",
+        f"rocprofv3 --pmc FETCH_SIZE -f csv -T -d $P/copy_fetch -o run -- "
         f"python3 bench.py --copy-probe-mib {COPY_PROBE_MIB}",
-        f"rocprofv3 --pmc WRITE_SIZE -f csv -T -d gpurun_out/prof/copy_write -o run -- "
+        f"rocprofv3 --pmc WRITE_SIZE -f csv -T -d $P/copy_write -o run -- "
         f"python3 bench.py --copy-probe-mib {COPY_PROBE_MIB}",
-        f"python3 bench.py --summarize-profile gpurun_out/prof --workload {workload}",
+        f"python3 bench.py --summarize-profile $P --workload {workload}",
         "```",
         "",
         "## Kernel trace (stats)",

@@ -30,7 +30,7 @@ the one it follows:
   result by the plain definition, which is what a flash-style kernel must
   equal up to rounding.
 
-Readings where the pages are silent (listed with the others in the design doc):
+Readings where the pages are silent:
 sigma defaults to 1/sqrt(Dn + Dr); the causal mask keeps key j for query i iff
 j <= i in sequence-local indices (queries and keys share one length per
 sequence); GQA maps query head h to KV head h // (Hq / Hkv); the rope parts are
