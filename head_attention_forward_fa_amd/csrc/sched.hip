@@ -18,10 +18,10 @@
 //     XCD, largest first in a snake order so the queues carry equal work.
 //     A queue runs chunk by chunk (a chunk: consecutive groups), a chunk in
 //     rounds: round k holds the k-th longest q-tile of each of its groups
-//     (causal cost grows with the tile index).  Causal: one chunk per
-//     queue, so the queue drains with short items and the CUs finish close
-//     together.  Non-causal: one group per chunk (equal costs; a group's
-//     items share their K/V in the XCD's L2).
+//     (causal cost grows with the tile index).  Causal: chunks of 8
+//     groups, so each chunk, and the queue, drains with short items and the
+//     CUs finish close together.  Non-causal: one group per chunk (equal
+//     costs; a group's items share their K/V in the XCD's L2).
 //   * the attention kernel is launched with about (CUs x resident
 //     workgroups) workgroups; each pops items from queue blockIdx % 8 with
 //     one atomic add, then helps the other queues once its own is empty.
