@@ -225,7 +225,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   // mha_fwd: key splits of its own where the longest items would set the
   // run time, partials in the workspace (laid out for batch x max_seqlen
   // tokens; the merge stops at the real total, cu_seqlens[batch])
-  const bool auto_split = num_splits == 1 && o_part == nullptr && var->launch_split != nullptr;
+  // (also under mha_fwd_splitkv with num_splits = 1, which is mha_fwd exactly;
+  // its partial buffers are not used then)
+  const bool auto_split = num_splits == 1 && var->launch_split != nullptr;
   size_t part_bytes = 0;
   if (auto_split) {
     const int sp = auto_splits(batch, max_seqlen, num_heads, causal, v_dim, var->block_m,

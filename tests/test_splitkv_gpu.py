@@ -82,12 +82,14 @@ def test_merged_and_partials_match_oracle(case):
         assert max_abs(opn[s][okt], po[okt]) <= TOL_O[dtype], f"split {s} O"
 
 
-def test_one_split_is_mha_fwd_and_runs_repeat():
-    inp = _inputs("bf16", [1, 129, 0, 517, 64], 8, 2, 128, 0, 128, True)
+@pytest.mark.parametrize("lens,hq,hkv", [([1, 129, 0, 517, 64], 8, 2),
+                                         ([2048, 300], 2, 2)])  # the second: mha_fwd splits itself
+def test_one_split_is_mha_fwd_and_runs_repeat(lens, hq, hkv):
+    inp = _inputs("bf16", lens, hq, hkv, 128, 0, 128, True)
     t = device_tensors(inp)
     o1, l1 = _run(inp, t, 1)
-    o2, l2 = _run(inp, t, 1, torch.empty((1, inp.total_tokens, 8, 128), device="cuda"),
-                  torch.empty((1, 8, inp.total_tokens), device="cuda"))
+    o2, l2 = _run(inp, t, 1, torch.empty((1, inp.total_tokens, hq, 128), device="cuda"),
+                  torch.empty((1, hq, inp.total_tokens), device="cuda"))
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     a = _run(inp, t, 3)
     b = _run(inp, t, 3)
