@@ -178,16 +178,17 @@ def test_scheduler_visits_every_item_once(block_m, grid):
     assert np.array_equal(visits.cpu().numpy(), want)
 
 
-def test_scheduler_many_groups_index_mode():
+@pytest.mark.parametrize("causal", [False, True])
+def test_scheduler_many_groups_index_mode(causal):
     # more (sequence, KV head) groups than the prepass ranks in LDS: the
     # contiguous-range queue assignment must still cover every item once
     from head_attention_forward_fa_amd import mha_sched_visit
     rng = np.random.default_rng(9)
-    lens = rng.integers(0, 300, size=700)
+    lens = rng.integers(0, 600, size=700)
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     hq, hkv = 8, 4
     mx = int(lens.max())
-    visits = mha_sched_visit(torch.from_numpy(cu).cuda(), mx, hq, hkv, False, 256, 0)
+    visits = mha_sched_visit(torch.from_numpy(cu).cuda(), mx, hq, hkv, causal, 256, 0)
     torch.cuda.synchronize()
     tiles = (mx + 255) // 256
     want = np.zeros((hq, len(lens), tiles), dtype=np.int32)
