@@ -639,14 +639,18 @@ struct MfmaKernel {
     const uint32_t sbase = lds_addr_of(smem);
     const uint32_t junk = sbase + C::JUNK;
 
-    // wave 0 runs the work-item source; the next item's table entry is read
-    // while the current item's first blocks load and published at the first
-    // barrier after that
+    // wave FW runs the work-item source.  It belongs to group 1, which
+    // issues no DMA, so its vector-memory counter holds only its own loads.
+    // The next item is reserved three blocks before the current item's end
+    // and its table entry read one block before it: the choice is made
+    // late (list scheduling over the queue order, so the CUs finish close
+    // together) and neither round trip sits between two items.
+    constexpr int FW = C::WAVES / 2;
     Fetcher fetch;
-    if (wave == 0) {
+    if (wave == FW) {
       fetch.init(p.sched);
-      const i32x4 e0 = fetch.take(p.sched, p.table);
-      if (tid == 0) s_item[0] = e0;
+      const i32x4 e0 = fetch.resolve(p.sched, p.table);
+      if (lane == 0) s_item[0] = e0;
     }
     for (int it = 0;; ++it) {
       __syncthreads();
@@ -656,8 +660,6 @@ struct MfmaKernel {
                                             __builtin_amdgcn_readfirstlane(s_item[it & 1][2]),
                                             __builtin_amdgcn_readfirstlane(s_item[it & 1][3])});
       if (wi.L < 0) break;
-      i32x4 nxt;
-      if (wave == 0) nxt = fetch.take(p.sched, p.table);
       const int s0 = wi.s0;
       const int L = wi.L;
       const int g = wi.h / p.group;
@@ -683,6 +685,8 @@ struct MfmaKernel {
       const int last_sub = n_sub_all - 1;                // the one that takes the mask
       const int n_sub = SPLIT ? min(n_sub_all, 2 * jhi) : n_sub_all;  // sub-tiles 2 jlo .. n_sub - 1 here
       const bool has_sub = n_sub > 2 * jlo;
+      const int j_res = max(jlo, jhi - 3), j_get = max(jlo, jhi - 1);
+      i32x4 nxt = {0, -1, 0, 0};
       const int lim = p.causal ? min(L - 1, qi) : L - 1;  // last key visible to this lane
 
       // Q fragments (B operand): lane -> query qi, 8 (bf16) or 32 (fp8)
@@ -752,7 +756,6 @@ struct MfmaKernel {
         for (int t = jlo - C::KLEAD; t < jlo + (C::KLEAD == 3 ? -1 : 0); ++t)
           dma_ops<0, C::N_OPS>(blk(t), dl, junk, wave);
       wait_vm<0>();
-      if (tid == 0) s_item[(it + 1) & 1] = nxt;
       __syncthreads();
       if (has_sub) {
         const uint32_t ks0 = sbase + (uint32_t)(jlo % C::NKS) * C::KSLOT;
@@ -833,9 +836,28 @@ struct MfmaKernel {
         for (; j < j_steady; ++j) block(P0{}, N{}, j);
         for (; j < jhi; ++j) block(P0{}, Y{}, j);
       } else {
+        auto fetch_at = [&](int j) {
+          if (wave == FW) {
+            if (j == j_res) fetch.reserve(p.sched);
+            if (j == j_get) nxt = fetch.resolve(p.sched, p.table);
+          }
+        };
         int j = jlo;
-        for (; j < j_steady; ++j) block(P1{}, N{}, j);
-        for (; j < jhi; ++j) block(P1{}, Y{}, j);
+        for (; j < j_steady; ++j) {
+          fetch_at(j);
+          block(P1{}, N{}, j);
+        }
+        for (; j < jhi; ++j) {
+          fetch_at(j);
+          block(P1{}, Y{}, j);
+        }
+        if (wave == FW) {
+          if (jhi <= jlo) {  // no blocks in this item (an empty key range)
+            fetch.reserve(p.sched);
+            nxt = fetch.resolve(p.sched, p.table);
+          }
+          if (lane == 0) s_item[(it + 1) & 1] = nxt;
+        }
       }
       // the last batches requested nothing; drain, and let group 1 finish
       // its last products, before the rings are reused for the output

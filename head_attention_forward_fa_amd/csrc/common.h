@@ -142,13 +142,18 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // the same path; only lane 0 touches the counters).  Queue choice is
 // XCD-aware: workgroup i is dispatched to XCD i % 8, so it drains queue
 // i % 8 first (whose items share K/V and therefore that XCD's L2), then the
-// others.  The index of the following item is reserved (atomic add) one
-// item ahead and read back only at the next take(); take() itself only
-// issues the table read, whose value the caller needs later.  So neither
-// memory round trip has to sit between two items.
+// others.  Two ways to drive it:
+//   take()              the entry of the index reserved before, and a
+//                       reservation of the next one (one item ahead);
+//   reserve(), resolve() the reservation and the entry read as two steps,
+//                       which a kernel places near the end of its current
+//                       item, so that the next item is chosen late (the
+//                       queue then deals like a list scheduler over the
+//                       queue order) while neither memory round trip sits
+//                       between two items.
 struct Fetcher {
   int queue, tried, cnt, base;  // wave-uniform
-  int pend;                     // lane 0: the reserved index (in flight until the next take)
+  int pend;                     // lane 0: the reserved index (in flight until resolved)
 
   __device__ __forceinline__ void open_queue(const SchedState* st) {
     cnt = __builtin_amdgcn_readfirstlane(st->q[queue].count);
@@ -164,9 +169,20 @@ struct Fetcher {
     open_queue(st);
     reserve(st);
   }
-  // Entry of the reserved index (moving on to the next queue once this one
-  // is exhausted) and a reservation of the index after it; L = -1 when every
-  // queue is exhausted.
+  // Entry of the reserved index, moving on to the next queue (and reserving
+  // there) while this one is exhausted; L = -1 when every queue is.
+  __device__ __forceinline__ i32x4 resolve(SchedState* st, const i32x4* table) {
+    for (;;) {
+      const int idx = __builtin_amdgcn_readfirstlane(pend);
+      if (idx < cnt) return table[base + idx];
+      if (++tried >= kNumXcd) return i32x4{0, -1, 0, 0};
+      queue = (queue + 1) % kNumXcd;
+      open_queue(st);
+      reserve(st);
+    }
+  }
+  // resolve(), plus a reservation of the next index once an entry is found
+  // (issued without waiting for the entry's table read)
   __device__ __forceinline__ i32x4 take(SchedState* st, const i32x4* table) {
     for (;;) {
       const int idx = __builtin_amdgcn_readfirstlane(pend);
