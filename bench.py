@@ -127,8 +127,10 @@ class HipEvents:
         self.hip.hipEventDestroy(ev)
 
 
-def peak_for(inp) -> float:
-    if inp.dtype == "fp8":
+def peak_for(inp, fast_accum: bool = False) -> float:
+    # fp8 codes decoded to bfloat16 (the default) run every product at the
+    # bf16 rate
+    if inp.dtype == "fp8" and fast_accum:
         # the nope QK^T runs at the fp8 rate, a rope QK^T and PV at the bf16
         # rate: time-weighted peak
         dn, dr, dv = inp.head_dim_nope, inp.head_dim_rope, inp.v_dim
@@ -404,6 +406,10 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=1,
                     help="split-KV: cut every query tile's keys into this many work items "
                          "(mha_fwd_splitkv) and merge")
+    ap.add_argument("--fp8-fast-accum", action="store_true",
+                    help="fp8 workloads: Q K^T on the fp8 matrix instruction "
+                         "(MHA_DTYPE_FP8_E4M3_FASTACC, reduced accumulation precision) instead "
+                         "of the exact default")
     ap.add_argument("--op", default="attention", choices=("attention", "quantize"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -471,10 +477,12 @@ def main(argv=None):
                     lse_partial=torch.empty((a.splits, inp.num_heads, inp.total_tokens),
                                             dtype=torch.float32, device=dev))
 
+    fast = bool(a.fp8_fast_accum and inp.dtype == "fp8")
+
     def step():
         mha_fwd(q, k, v, causal=inp.causal, cu_seqlens=cu, max_seqlen=inp.max_seqlen,
                 q_rope=qr, k_rope=kr, q_scale=qs, k_scale=ks,
-                softmax_scale=inp.softmax_scale, out=o, lse=lse, **part)
+                softmax_scale=inp.softmax_scale, out=o, lse=lse, fp8_fast_accum=fast, **part)
 
     for _ in range(a.warmup):
         step()
@@ -507,8 +515,8 @@ def main(argv=None):
     flops = mi.attention_flops(inp)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kmean * 1e-3) / 1e12
-    peak = peak_for(inp)
-    traffic = traffic_from_profile(inp.name)
+    peak = peak_for(inp, fast)
+    traffic = traffic_from_profile(inp.name + ("_fastacc" if fast else ""))
     print(f"[bench] {ms_per_step * 1e3:.1f} us/step, attention kernel mean {kmean * 1e3:.1f} us "
           f"(min {min(kernel_ms) * 1e3:.1f}), {value:.1f} TFLOP/s, {100 * achieved / peak:.1f}% "
           f"of {peak:.0f}", file=sys.stderr, flush=True)
@@ -529,10 +537,12 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 QK / bf16 PV", "f32": "f32"}[inp.dtype],
+        "dtype": {"bf16": "bf16", "f32": "f32",
+                  "fp8": ("fp8-e4m3 QK / bf16 PV" if fast
+                          else "fp8-e4m3 Q/K decoded to bf16 for QK, bf16 PV")}[inp.dtype],
         "data": "synthetic",
         "config": {
-            "workload": inp.name,
+            "workload": inp.name + ("_fastacc" if fast else ""),
             "batch": inp.batch,
             "num_heads": inp.num_heads,
             "num_kv_heads": inp.num_kv_heads,

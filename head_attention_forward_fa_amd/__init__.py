@@ -9,5 +9,5 @@ from .mha import (  # noqa: F401
     mha_quantize_fp8, mha_sched_visit,
 )
 from ._native import (  # noqa: F401
-    MHA_DTYPE_BF16, MHA_DTYPE_F32, MHA_DTYPE_FP8_E4M3, MhaError, load,
+    MHA_DTYPE_BF16, MHA_DTYPE_F32, MHA_DTYPE_FP8_E4M3, MHA_DTYPE_FP8_E4M3_FASTACC, MhaError, load,
 )

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmha_fwd.
 MHA_DTYPE_F32 = 0
 MHA_DTYPE_BF16 = 1
 MHA_DTYPE_FP8_E4M3 = 2
+MHA_DTYPE_FP8_E4M3_FASTACC = 3
 
 MHA_OK = 0
 MHA_ERR_INVALID_ARG = 1

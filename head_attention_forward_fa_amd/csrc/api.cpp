@@ -23,7 +23,9 @@ const Variant* find_variant(int dtype, int dn, int dr, int dv) {
     case MHA_DTYPE_BF16:
       return find_variant_bf16(dn, dr, dv);
     case MHA_DTYPE_FP8_E4M3:
-      return find_variant_fp8(dn, dr, dv);
+      return find_variant_fp8(dn, dr, dv, false);
+    case MHA_DTYPE_FP8_E4M3_FASTACC:
+      return find_variant_fp8(dn, dr, dv, true);
     default:
       return nullptr;
   }
@@ -197,7 +199,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   if (head_dim_nope < 1 || head_dim_rope < 0 || v_dim < 1)
     return fail(MHA_ERR_INVALID_ARG, "head dims must be positive (rope >= 0)");
   if (causal != 0 && causal != 1) return fail(MHA_ERR_INVALID_ARG, "causal must be 0 or 1");
-  if (dtype != MHA_DTYPE_F32 && dtype != MHA_DTYPE_BF16 && dtype != MHA_DTYPE_FP8_E4M3)
+  if (dtype != MHA_DTYPE_F32 && dtype != MHA_DTYPE_BF16 && dtype != MHA_DTYPE_FP8_E4M3 &&
+      dtype != MHA_DTYPE_FP8_E4M3_FASTACC)
     return fail(MHA_ERR_INVALID_ARG, "unknown dtype");
   if (std::isnan(softmax_scale) || std::isinf(softmax_scale))
     return fail(MHA_ERR_INVALID_ARG, "softmax_scale must be finite");
@@ -214,7 +217,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
     return fail(MHA_ERR_INVALID_ARG, "q_rope and k_rope must both be given or both NULL");
   if ((head_dim_rope > 0) != (q_rope != nullptr))
     return fail(MHA_ERR_INVALID_ARG, "rope pointers must be given iff head_dim_rope > 0");
-  const bool fp8 = dtype == MHA_DTYPE_FP8_E4M3;
+  const bool fp8 = dtype == MHA_DTYPE_FP8_E4M3 || dtype == MHA_DTYPE_FP8_E4M3_FASTACC;
   if (fp8 != (q_scale != nullptr) || fp8 != (k_scale != nullptr))
     return fail(MHA_ERR_INVALID_ARG, "q_scale and k_scale must be given iff dtype is FP8_E4M3");
 

@@ -75,10 +75,19 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-template <int DN_, int DR_, int DV_, bool FP8_>
+// FP8_: Q/K nope parts are OCP E4M3 codes with per-token scales.  F8MMA_:
+// their products run on the fp8 matrix instruction, whose accumulation keeps
+// only about 13 bits below the largest of the 64 products of one
+// instruction (measured on gfx950: error up to 2^-13 of the sum of the
+// products' magnitudes, where a bf16 product of the same values errs by
+// 2^-22); without it the codes are decoded to bfloat16 (exact: E4M3 has 3
+// mantissa bits and exponents well inside bfloat16's range) and the
+// products run on the bf16 instruction with float32-grade accumulation.
+template <int DN_, int DR_, int DV_, bool FP8_, bool F8MMA_ = FP8_>
 struct MfmaCfg {
   static constexpr int DN = DN_, DR = DR_, DV = DV_;
   static constexpr bool FP8 = FP8_;
+  static constexpr bool F8MMA = FP8_ && F8MMA_;
   // fp8 nope with a bfloat16 rope part: the per-token scales multiply the
   // nope product only, so the two products accumulate separately
   static constexpr bool MIXED = FP8 && DR > 0;
@@ -109,7 +118,7 @@ struct MfmaCfg {
   static constexpr int LDS = JUNK + 1024;
   static constexpr int OCC = 1;              // one workgroup (8 waves) per CU
   static constexpr int O_ROW = DV * 2 + 16;  // epilogue staging row stride
-  static constexpr int QK_STEPS = FP8 ? DN / 64 : DN / 16;  // nope MFMA k-steps
+  static constexpr int QK_STEPS = F8MMA ? DN / 64 : DN / 16;  // nope MFMA k-steps
   static constexpr int ROPE_STEPS = DR / 16;
   static constexpr int S_STEPS = QK_STEPS + ROPE_STEPS;  // S products per sub-tile
   static constexpr int DV_TILES = DV / 32;
@@ -180,7 +189,7 @@ __device__ __forceinline__ void wait_vm() {
 
 template <class C>
 struct MfmaKernel {
-  using QFrag = typename std::conditional<C::FP8, i32x8, bf16x8>::type;
+  using QFrag = typename std::conditional<C::F8MMA, i32x8, bf16x8>::type;
 
   // ------------------------------------------------------------ staging
 
@@ -400,7 +409,7 @@ struct MfmaKernel {
   static __device__ __forceinline__ Lanes lanes_of(int lane) {
     const int lane32 = lane & 31, hf = lane >> 5;
     Lanes ln;
-    ln.k = lane32 * C::K_RP + (C::FP8 ? 32 : 16) * hf;
+    ln.k = lane32 * C::K_RP + (C::F8MMA ? 32 : C::FP8 ? 8 : 16) * hf;
     ln.r = lane32 * C::R_RP + 16 * hf;
     const int grp = lane >> 4, s = lane & 15;
     const int k1 = 4 * (grp >> 1) + (s >> 2);  // key row of the first read (u = 0)
@@ -416,8 +425,26 @@ struct MfmaKernel {
   // A operand of S product s of a 32-key sub-tile, from the per-lane K
   // (nope) and rope addresses of the sub-tile: nope steps first, then rope
   // steps.  Row pitch is K_RP.
+  // 8 E4M3 codes (depth order) -> 8 bfloat16 values, exactly
+  static __device__ __forceinline__ bf16x8 dec8(i32x2 x) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  }
   static __device__ __forceinline__ QFrag s_frag(uint32_t kt, uint32_t rt, int s) {
-    if constexpr (C::FP8) {
+    if constexpr (C::FP8 && !C::F8MMA) {
+      // E4M3 rows at pitch K_RP: step s covers depth 16 s .. 16 s + 15, 8
+      // bytes per lane half
+      if (s < C::QK_STEPS) {
+        const i32x2 x =
+            *reinterpret_cast<const __attribute__((address_space(3))) i32x2*>(lp(kt) + 16 * s);
+        return dec8(x);
+      }
+      return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+          lp(rt) + 32 * (s - C::QK_STEPS));
+    } else if constexpr (C::FP8) {
       const i32x4 a0 = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
           lp(kt) + 64 * s);
       const i32x4 a1 = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
@@ -439,7 +466,7 @@ struct MfmaKernel {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
   }
   static __device__ __forceinline__ f32x16 s_mfma(const QFrag& a, const QFrag& b, f32x16 acc) {
-    if constexpr (C::FP8)
+    if constexpr (C::F8MMA)
       return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
     else
       return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
@@ -607,7 +634,7 @@ struct MfmaKernel {
       if constexpr (k < NS) {
         constexpr bool PV = k < 2 * NPAIR ? (k % 2 == 0) : (C::NPV > C::S_STEPS);
         constexpr int idx = k < 2 * NPAIR ? k / 2 : k - NPAIR;
-        __builtin_amdgcn_sched_group_barrier(0x100, PV ? 2 : (C::FP8 && idx < C::QK_STEPS ? 2 : 1),
+        __builtin_amdgcn_sched_group_barrier(0x100, PV ? 2 : (C::F8MMA && idx < C::QK_STEPS ? 2 : 1),
                                              0);
       }
       if constexpr (k >= RA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -652,6 +679,68 @@ struct MfmaKernel {
       const i32x4 e0 = fetch.resolve(p.sched, p.table);
       if (lane == 0) s_item[0] = e0;
     }
+    // Q fragments (B operand): lane -> query qi, 8 (bf16) or 32 (fp8)
+    // consecutive depth elements per step and lane half; rope steps follow
+    // the nope steps.  cq: the multiplier of S in the exponent (log2
+    // domain), kept >= FLT_MIN so that a masked -inf score stays -inf (a
+    // zero q_scale row then gives the uniform distribution over its visible
+    // keys, as 0 * S does).
+    constexpr int NQF = C::MIXED ? C::QK_STEPS : C::S_STEPS;
+    constexpr int NQR = C::MIXED ? C::ROPE_STEPS : 1;  // mixed layout: the rope steps
+    auto load_q = [&](const WorkItem& wi, QFrag* qf, bf16x8* qr, float& cq) {
+      const int qi = wi.qt * C::BM + wave * 32 + lane32;
+      const bool qvalid = qi < wi.L;
+      const size_t qrow = (size_t)(wi.s0 + qi) * p.num_heads + wi.h;
+#pragma unroll
+      for (int s = 0; s < C::S_STEPS; ++s) {
+        if constexpr (C::MIXED) {
+          if (s >= C::QK_STEPS) {
+            i32x4 x = {0, 0, 0, 0};
+            if (qvalid)
+              x = *reinterpret_cast<const i32x4*>(
+                  qrp + (qrow * C::DR + (s - C::QK_STEPS) * 16 + 8 * hf) * 2);
+            qr[s - C::QK_STEPS] = __builtin_bit_cast(bf16x8, x);
+            continue;
+          }
+        }
+        if constexpr (C::FP8 && !C::F8MMA) {
+          i32x2 x = {0, 0};
+          if (qvalid) x = *reinterpret_cast<const i32x2*>(qp + qrow * C::DN + s * 16 + 8 * hf);
+          qf[s] = dec8(x);
+        } else if constexpr (C::FP8) {
+          i32x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+          if (qvalid) {
+            const i32x4* src =
+                reinterpret_cast<const i32x4*>(qp + qrow * C::DN + s * 64 + 32 * hf);
+            const i32x4 a0 = src[0], a1 = src[1];
+            x = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          }
+          qf[s] = x;
+        } else {
+          i32x4 x = {0, 0, 0, 0};
+          if (qvalid) {
+            const char* src = s < C::QK_STEPS
+                                  ? qp + (qrow * C::DN + s * 16 + 8 * hf) * 2
+                                  : qrp + (qrow * C::DR + (s - C::QK_STEPS) * 16 + 8 * hf) * 2;
+            x = *reinterpret_cast<const i32x4*>(src);
+          }
+          qf[s] = __builtin_bit_cast(bf16x8, x);
+        }
+      }
+      cq = p.scale_log2;
+      if (C::FP8 && qvalid) cq *= p.q_scale[qrow];
+      if (!(cq >= 1.17549435e-38f)) cq = 1.17549435e-38f;
+    };
+    // Without a rope part, the next item's Q loads are issued as soon as
+    // the next item is known (after the current item's last products),
+    // ahead of the current item's output stores, so that their latency
+    // overlaps the epilogue.  (With a rope part the longer live range
+    // costs more than it saves.)
+    constexpr bool EARLY_Q = C::DR == 0;
+    // (the fragments live across items only when they are loaded early)
+    QFrag qf_x[EARLY_Q ? NQF : 1];
+    bf16x8 qr_x[EARLY_Q ? NQR : 1];
+    float cq_x = 0.f;
     for (int it = 0;; ++it) {
       __syncthreads();
       // the item is the same for the whole workgroup: keep it in SGPRs
@@ -691,47 +780,56 @@ struct MfmaKernel {
 
       // Q fragments (B operand): lane -> query qi, 8 (bf16) or 32 (fp8)
       // consecutive depth elements per step and lane half; rope steps follow
-      // the nope steps.
-      QFrag qf[C::MIXED ? C::QK_STEPS : C::S_STEPS];
-      bf16x8 qr[C::MIXED ? C::ROPE_STEPS : 1];  // mixed layout: the rope steps
+      // the nope steps.  cq: see load_q.
+      QFrag qf_i[EARLY_Q ? 1 : NQF];
+      bf16x8 qr_i[EARLY_Q ? 1 : NQR];
+      QFrag* qf = EARLY_Q ? qf_x : qf_i;
+      bf16x8* qr = EARLY_Q ? qr_x : qr_i;
+      if (EARLY_Q && it == 0) load_q(wi, qf_x, qr_x, cq_x);
+      if constexpr (!EARLY_Q) {
 #pragma unroll
-      for (int s = 0; s < C::S_STEPS; ++s) {
-        if constexpr (C::MIXED) {
-          if (s >= C::QK_STEPS) {
+        for (int s = 0; s < C::S_STEPS; ++s) {
+          if constexpr (C::MIXED) {
+            if (s >= C::QK_STEPS) {
+              i32x4 x = {0, 0, 0, 0};
+              if (qvalid)
+                x = *reinterpret_cast<const i32x4*>(
+                    qrp + (qrow * C::DR + (s - C::QK_STEPS) * 16 + 8 * hf) * 2);
+              qr_i[s - C::QK_STEPS] = __builtin_bit_cast(bf16x8, x);
+              continue;
+            }
+          }
+          if constexpr (C::FP8 && !C::F8MMA) {
+            i32x2 x = {0, 0};
+            if (qvalid) x = *reinterpret_cast<const i32x2*>(qp + qrow * C::DN + s * 16 + 8 * hf);
+            qf_i[s] = dec8(x);
+          } else if constexpr (C::FP8) {
+            i32x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (qvalid) {
+              const i32x4* src =
+                  reinterpret_cast<const i32x4*>(qp + qrow * C::DN + s * 64 + 32 * hf);
+              const i32x4 a0 = src[0], a1 = src[1];
+              x = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            }
+            qf_i[s] = x;
+          } else {
             i32x4 x = {0, 0, 0, 0};
-            if (qvalid)
-              x = *reinterpret_cast<const i32x4*>(
-                  qrp + (qrow * C::DR + (s - C::QK_STEPS) * 16 + 8 * hf) * 2);
-            qr[s - C::QK_STEPS] = __builtin_bit_cast(bf16x8, x);
-            continue;
+            if (qvalid) {
+              const char* src = s < C::QK_STEPS
+                                    ? qp + (qrow * C::DN + s * 16 + 8 * hf) * 2
+                                    : qrp + (qrow * C::DR + (s - C::QK_STEPS) * 16 + 8 * hf) * 2;
+              x = *reinterpret_cast<const i32x4*>(src);
+            }
+            qf_i[s] = __builtin_bit_cast(bf16x8, x);
           }
-        }
-        if constexpr (C::FP8) {
-          i32x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-          if (qvalid) {
-            const i32x4* src =
-                reinterpret_cast<const i32x4*>(qp + qrow * C::DN + s * 64 + 32 * hf);
-            const i32x4 a0 = src[0], a1 = src[1];
-            x = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          }
-          qf[s] = x;
-        } else {
-          i32x4 x = {0, 0, 0, 0};
-          if (qvalid) {
-            const char* src = s < C::QK_STEPS
-                                  ? qp + (qrow * C::DN + s * 16 + 8 * hf) * 2
-                                  : qrp + (qrow * C::DR + (s - C::QK_STEPS) * 16 + 8 * hf) * 2;
-            x = *reinterpret_cast<const i32x4*>(src);
-          }
-          qf[s] = __builtin_bit_cast(bf16x8, x);
         }
       }
-      // multiplier of S in the exponent (log2 domain); kept >= FLT_MIN so
-      // that a masked -inf score stays -inf (a zero q_scale row then gives
-      // the uniform distribution over its visible keys, as 0 * S does)
-      float cq = p.scale_log2;
-      if (C::FP8 && qvalid) cq *= p.q_scale[qrow];
-      if (!(cq >= 1.17549435e-38f)) cq = 1.17549435e-38f;
+      float cq = cq_x;
+      if constexpr (!EARLY_Q) {
+        cq = p.scale_log2;
+        if (C::FP8 && qvalid) cq *= p.q_scale[qrow];
+        if (!(cq >= 1.17549435e-38f)) cq = 1.17549435e-38f;
+      }
 
       State w;
 #pragma unroll
@@ -864,6 +962,14 @@ struct MfmaKernel {
       // staging
       wait_vm<0>();
       __syncthreads();
+      if constexpr (EARLY_Q) {
+        const WorkItem nw =
+            decode_item(i32x4{__builtin_amdgcn_readfirstlane(s_item[(it + 1) & 1][0]),
+                              __builtin_amdgcn_readfirstlane(s_item[(it + 1) & 1][1]),
+                              __builtin_amdgcn_readfirstlane(s_item[(it + 1) & 1][2]),
+                              __builtin_amdgcn_readfirstlane(s_item[(it + 1) & 1][3])});
+        if (nw.L >= 0) load_q(nw, qf_x, qr_x, cq_x);
+      }
 
       // ---- epilogue
       const float lt = half_sum(w.l);

@@ -62,6 +62,6 @@ const Variant* find_variant(int dtype, int dn, int dr, int dv);
 // Per-family tables (defined next to each kernel family).
 const Variant* find_variant_f32(int dn, int dr, int dv);
 const Variant* find_variant_bf16(int dn, int dr, int dv);
-const Variant* find_variant_fp8(int dn, int dr, int dv);
+const Variant* find_variant_fp8(int dn, int dr, int dv, bool fast);
 
 }  // namespace mha

@@ -53,8 +53,15 @@ def mha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
             lse: Optional[torch.Tensor] = None,
             num_splits: int = 1,
             o_partial: Optional[torch.Tensor] = None,
-            lse_partial: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+            lse_partial: Optional[torch.Tensor] = None,
+            fp8_fast_accum: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Fused attention forward; returns (o, lse).
+
+    fp8_fast_accum (fp8 inputs only) selects MHA_DTYPE_FP8_E4M3_FASTACC: Q K^T
+    on the fp8 matrix instruction (twice the rate of the exact default, which
+    decodes the codes to bfloat16), whose accumulation keeps about 13 bits
+    below the largest product, so the LSE of rows with large scores can be
+    off by more than 1e-3.
 
     num_splits > 1 runs mha_fwd_splitkv: the keys of every query tile are cut
     into that many ranges run as separate work items, then merged
@@ -68,6 +75,8 @@ def mha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     [Hq, T] float32 (natural log).  fp8: q, k as float8_e4m3fn (or uint8
     codes) with q_scale [T, Hq] and k_scale [T, Hkv] float32; v bf16.
     """
+    if fp8_fast_accum and q.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise ValueError("fp8_fast_accum applies to fp8 inputs only")
     dense = q.dim() == 4
     if dense:
         if cu_seqlens is not None:
@@ -91,6 +100,8 @@ def mha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU device")
     code = _dtype_code(qf)
+    if fp8_fast_accum:
+        code = nat.MHA_DTYPE_FP8_E4M3_FASTACC
     T, Hq, Dn = qf.shape
     Hkv, Dv = kf.shape[1], vf.shape[2]
     Dr = 0 if qrf is None else qrf.shape[2]

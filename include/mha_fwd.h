@@ -45,11 +45,20 @@ extern "C" {
 /* Element types.  F32: q, k, v, q_rope, k_rope and o are float32.
  * BF16: all of them are bfloat16.  FP8_E4M3: q and k are OCP E4M3 codes
  * ("fn", largest finite 448) with float32 per-token scales; v, o are
- * bfloat16 (SM100AttentionSMem, Parameters: qkv_dtype, scale_dtype_). */
+ * bfloat16 (SM100AttentionSMem, Parameters: qkv_dtype, scale_dtype_).
+ * FP8_E4M3 decodes the codes to bfloat16 (exactly) for the Q K^T products,
+ * which the bf16 matrix instruction sums with float32-grade accuracy.
+ * FP8_E4M3_FASTACC takes the same inputs but runs Q K^T on the fp8 matrix
+ * instruction at twice the rate; that instruction sums its 64 products
+ * keeping only about 13 bits below the largest one (measured on gfx950:
+ * error up to 2^-13 of the sum of the products' magnitudes), so a score
+ * can be off by about 1e-4 of sigma * sum_d |q_d k_d|, and the LSE of rows
+ * with large scores by more than 1e-3. */
 typedef enum {
   MHA_DTYPE_F32 = 0,
   MHA_DTYPE_BF16 = 1,
-  MHA_DTYPE_FP8_E4M3 = 2
+  MHA_DTYPE_FP8_E4M3 = 2,
+  MHA_DTYPE_FP8_E4M3_FASTACC = 3
 } mha_dtype_t;
 
 typedef enum {
@@ -100,13 +109,14 @@ typedef enum {
  *   q_scale     [T, num_heads] float32, k_scale [T, num_kv_heads] float32:
  *               dequantisation scales, value = code * scale, one per (token,
  *               head) row, >= 0 (SM100AttentionSMem, Methods: q_scale_smem,
- *               k_scale_smem).  Required iff dtype == FP8_E4M3, else NULL.
+ *               k_scale_smem).  Required iff dtype is FP8_E4M3 or
+ *               FP8_E4M3_FASTACC, else NULL.
  *   stream      hipStream_t or NULL
  *
  * Compiled set (MHA_ERR_UNSUPPORTED otherwise):
  *   F32      (Dn, Dr, Dv) in {(64,0,64), (128,0,128), (128,64,128)}
  *   BF16     (Dn, Dr, Dv) in {(64,0,64), (128,0,128), (128,64,128)}
- *   FP8_E4M3 (Dn, Dr, Dv) in {(128,0,128), (128,64,128)}
+ *   FP8_E4M3, FP8_E4M3_FASTACC  (Dn, Dr, Dv) in {(128,0,128), (128,64,128)}
  *
  * Key splits of its own (BF16 and FP8_E4M3): where the longest work items
  * would set the run time (few, long items for the device's CUs, e.g. one

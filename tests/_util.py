@@ -34,13 +34,13 @@ def device_tensors(inp: Inputs, device="cuda:0"):
     )
 
 
-def run_gpu(inp: Inputs, device="cuda:0", tensors=None):
+def run_gpu(inp: Inputs, device="cuda:0", tensors=None, fp8_fast_accum=False):
     from head_attention_forward_fa_amd import mha_fwd
     t = tensors or device_tensors(inp, device)
     o, lse = mha_fwd(t["q"], t["k"], t["v"], causal=inp.causal, cu_seqlens=t["cu_seqlens"],
                      max_seqlen=inp.max_seqlen, q_rope=t["q_rope"], k_rope=t["k_rope"],
                      q_scale=t["q_scale"], k_scale=t["k_scale"],
-                     softmax_scale=inp.softmax_scale)
+                     softmax_scale=inp.softmax_scale, fp8_fast_accum=fp8_fast_accum)
     torch.cuda.synchronize()
     return o, lse
 
@@ -139,3 +139,31 @@ def split_key_ranges(cu_seqlens, causal: bool, num_splits: int, block_m: int = 2
                 lo[s, cu[b] + i] = b0 * block_n
                 hi[s, cu[b] + i] = b1 * block_n
     return lo, hi
+
+
+def fast_accum_lse_bound(inp: Inputs, rel: float = 2.0 ** -12):
+    """Per-row LSE error bound [Hq, T] for fp8 with the fp8 matrix
+    instruction: that instruction's sum of products errs by up to about
+    2^-13 of the sum of the products' magnitudes (measured on gfx950; rel
+    doubles it for margin), so each score errs by at most
+    rel * sigma * sum_d |q_d k_d| over the nope depth (the rope part runs on
+    the bf16 instruction), and an LSE, a softmax-weighted mean of its row's
+    scores to first order, by at most the largest of those over the visible
+    keys."""
+    q, k, _, _, _ = decoded(inp)
+    cu = inp.cu_seqlens.astype(np.int64)
+    group = inp.num_heads // inp.num_kv_heads
+    sigma = (inp.softmax_scale if inp.softmax_scale
+             else 1.0 / np.sqrt(inp.head_dim_nope + inp.head_dim_rope))
+    bound = np.zeros((inp.num_heads, inp.total_tokens))
+    for b in range(inp.batch):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        if s1 == s0:
+            continue
+        for h in range(inp.num_heads):
+            g = h // group
+            m = np.abs(q[s0:s1, h]) @ np.abs(k[s0:s1, g]).T
+            if inp.causal:
+                m = np.tril(m)
+            bound[h, s0:s1] = rel * sigma * m.max(axis=1)
+    return bound

@@ -56,6 +56,8 @@ BAD = [
     dict(causal=2), dict(dtype=7),
     dict(dtype=nat.MHA_DTYPE_FP8_E4M3),           # fp8 without scales
     dict(dtype=nat.MHA_DTYPE_FP8_E4M3, q_scale=FAKE),
+    dict(dtype=nat.MHA_DTYPE_FP8_E4M3_FASTACC),   # fast-accumulation fp8 without scales
+    dict(dtype=nat.MHA_DTYPE_FP8_E4M3_FASTACC, k_scale=FAKE),
     dict(q_scale=FAKE, k_scale=FAKE),             # scales with bf16
     dict(scale=math.nan), dict(scale=math.inf),
 ]
@@ -87,6 +89,7 @@ def test_supported_set():
         nat.MHA_DTYPE_F32: {(64, 0, 64), (128, 0, 128), (128, 64, 128)},
         nat.MHA_DTYPE_BF16: {(64, 0, 64), (128, 0, 128), (128, 64, 128)},
         nat.MHA_DTYPE_FP8_E4M3: {(128, 0, 128), (128, 64, 128)},
+        nat.MHA_DTYPE_FP8_E4M3_FASTACC: {(128, 0, 128), (128, 64, 128)},
     }
     for dt, shapes in want.items():
         for dn in (32, 64, 96, 128, 192, 256):
@@ -110,6 +113,15 @@ def test_set_kernel_events_validation():
     assert lib.mha_fwd_set_kernel_events(FAKE, None) == nat.MHA_ERR_INVALID_ARG
     assert lib.mha_fwd_set_kernel_events(None, FAKE) == nat.MHA_ERR_INVALID_ARG
     assert lib.mha_fwd_set_kernel_events(None, None) == nat.MHA_OK
+
+
+def test_python_binding_fast_accum_needs_fp8():
+    import torch
+    from head_attention_forward_fa_amd import mha_fwd
+    q = torch.zeros(2, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mha_fwd(q, q, q, cu_seqlens=torch.tensor([0, 2], dtype=torch.int32), max_seqlen=2,
+                fp8_fast_accum=True)
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -12,8 +12,8 @@ import pytest
 import torch
 
 import mha_inputs as mi
-from _util import (TOL_LSE, TOL_O, device_tensors, max_abs, oracle_full, oracle_rows,
-                   run_gpu, sample_tokens, to_f64)
+from _util import (TOL_LSE, TOL_O, device_tensors, fast_accum_lse_bound, max_abs, oracle_full,
+                   oracle_rows, run_gpu, sample_tokens, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,6 +40,13 @@ SMALL = [
     ("f32", [70], 2, 1, 128, 64, 128, True),
     ("f32", [130, 1], 2, 2, 64, 0, 64, True),
     ("f32", [130, 1], 2, 2, 64, 0, 64, False),
+    # more items than workgroups (about 1 000 against 256): every workgroup
+    # runs several items in a row, so whatever an item carries over to the
+    # next (its Q fragments, the fp8 q_scale multiplier, the next item's
+    # entry) is exercised
+    ("fp8", [300, 257, 40, 512] * 8, 16, 4, 128, 0, 128, True),
+    ("bf16", [300, 257, 40, 512] * 8, 16, 4, 128, 0, 128, True),
+    ("bf16", [300, 257, 40, 512] * 8, 16, 16, 128, 64, 128, True),
 ]
 
 
@@ -54,7 +61,12 @@ def _check(inp, o, lse, ref_o, ref_lse, tokens=None):
     return eo, el
 
 
-@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}x{c[3]}-{c[4]}+{c[5]}-{c[6]}-{'c' if c[7] else 'nc'}")
+def _case_id(c):
+    lens = c[1] if len(c[1]) <= 6 else f"{len(c[1])}seq"
+    return f"{c[0]}-{lens}-{c[2]}x{c[3]}-{c[4]}+{c[5]}-{c[6]}-{'c' if c[7] else 'nc'}"
+
+
+@pytest.mark.parametrize("case", SMALL, ids=_case_id)
 def test_small_cases_match_oracle(case):
     dt, lens, hq, hkv, dn, dr, dv, causal = case
     inp = mi.make_inputs(dtype=dt, seqlens=lens, num_heads=hq, num_kv_heads=hkv,
@@ -64,6 +76,35 @@ def test_small_cases_match_oracle(case):
     o, lse = run_gpu(inp)
     ref_o, ref_lse = oracle_full(inp)
     _check(inp, o, lse, ref_o, ref_lse)
+
+
+FAST = [
+    # dtype, lengths, Hq, Hkv, Dn, Dr, Dv, causal
+    ("fp8", [300, 50], 4, 4, 128, 0, 128, True),
+    ("fp8", [257, 0, 129], 8, 2, 128, 0, 128, False),
+    ("fp8", [333, 20], 4, 4, 128, 64, 128, True),
+    ("fp8", [300, 257, 40, 512] * 4, 16, 4, 128, 0, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", FAST, ids=_case_id)
+def test_fp8_fast_accum_within_its_bound(case):
+    """MHA_DTYPE_FP8_E4M3_FASTACC: O at the fp8 tolerance; LSE within the
+    per-row bound that the fp8 matrix instruction's accumulation precision
+    gives (fast_accum_lse_bound) plus the LSE tolerance."""
+    dt, lens, hq, hkv, dn, dr, dv, causal = case
+    inp = mi.make_inputs(dtype=dt, seqlens=lens, num_heads=hq, num_kv_heads=hkv,
+                         head_dim_nope=dn, head_dim_rope=dr, v_dim=dv, causal=causal,
+                         seed=7, name=str(case))
+    print("fast-accum case", case, flush=True)
+    o, lse = run_gpu(inp, fp8_fast_accum=True)
+    ref_o, ref_lse = oracle_full(inp)
+    o64, lse64 = to_f64(o), to_f64(lse)
+    assert np.all(np.isfinite(o64)) and np.all(np.isfinite(lse64))
+    assert max_abs(o64, ref_o) <= TOL_O["fp8"]
+    err = np.abs(lse64 - ref_lse)
+    bound = fast_accum_lse_bound(inp) + TOL_LSE
+    assert np.all(err <= bound), f"worst excess {np.max(err - bound)}"
 
 
 def test_fp32_dense_workload_full():
