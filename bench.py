@@ -135,6 +135,8 @@ def peak_for(inp, fast_accum: bool = False) -> float:
         # rate: time-weighted peak
         dn, dr, dv = inp.head_dim_nope, inp.head_dim_rope, inp.v_dim
         return (dn + dr + dv) / (dn / PEAK_TFLOPS["fp8"] + (dr + dv) / PEAK_TFLOPS["bf16"])
+    if inp.dtype == "fp8":
+        return PEAK_TFLOPS["bf16"]
     return PEAK_TFLOPS[inp.dtype]
 
 
