@@ -95,8 +95,14 @@ struct MfmaCfg {
   static constexpr int BN = kBlockN_Mfma;  // 64 keys per block
   static constexpr int WAVES = BM / 32;    // 8 waves, two per SIMD
   static constexpr int THREADS = WAVES * kWave;
+  // SD: exact fp8 without a rope part decodes each K block once, for the
+  // whole workgroup: the fp8 rows land in a staging ring and are written
+  // back as bfloat16 rows into the K ring, which the products then read as
+  // in the bf16 kernel
+  static constexpr bool SD = FP8 && !F8MMA && DR == 0;
   static constexpr int EB = FP8 ? 1 : 2;   // bytes per Q/K nope element
-  static constexpr int K_RB = DN * EB;     // bytes per K nope row
+  static constexpr int K_HB = DN * EB;     // bytes per K nope row in HBM
+  static constexpr int K_RB = SD ? DN * 2 : K_HB;  // bytes per K nope row in a K slot
   static constexpr int R_RB = DR * 2;      // bytes per K rope row
   static constexpr int V_RB = DV * 2;      // bytes per V row
   // LDS: [K slots | V slots | sink]; block b lives in K slot b % NKS and V
@@ -110,10 +116,17 @@ struct MfmaCfg {
   static constexpr int KS_OFF = R_OFF + BN * R_RP;     // inside a K slot
   static constexpr int KSLOT = (KS_OFF + (FP8 ? 256 : 0) + 255) / 256 * 256;
   static constexpr int VSLOT = BN * V_RB;
-  // 4 K slots when they fit next to the V ring, else 3 (the rope layout)
-  static constexpr int NKS = 4 * KSLOT + NVS * BN * V_RB + 1024 + 64 <= 160 * 1024 ? 4 : 3;
-  static constexpr int KLEAD = NKS - 1;  // blocks between a K block's request and its use
-  static constexpr int V_BASE = NKS * KSLOT;
+  // SD staging slot: fp8 rows (unpadded), k_scale
+  static constexpr int NSS = SD ? 3 : 0;
+  static constexpr int SSLOT = SD ? BN * K_HB + 256 : 0;
+  // 4 K slots when they fit next to the V ring, else 3 (the rope layout);
+  // SD: 3 (a decoded block is written one block before its first use)
+  static constexpr int NKS =
+      SD ? 3 : 4 * KSLOT + NVS * BN * V_RB + 1024 + 64 <= 160 * 1024 ? 4 : 3;
+  // blocks between a K block's request and its use (SD: its decode)
+  static constexpr int KLEAD = SD ? 4 : NKS - 1;
+  static constexpr int S_BASE = NKS * KSLOT;
+  static constexpr int V_BASE = S_BASE + NSS * SSLOT;
   static constexpr int JUNK = V_BASE + NVS * VSLOT;  // 1 KiB sink for padding DMA ops
   static constexpr int LDS = JUNK + 1024;
   static constexpr int OCC = 1;              // one workgroup (8 waves) per CU
@@ -132,7 +145,7 @@ struct MfmaCfg {
   // that does not exist read nothing (empty buffer range) and land in the
   // JUNK sink, so one vmcnt(N_OPS) wait fits every wave and every block.
   static constexpr int DW = WAVES / 2;
-  static constexpr int K_INST = BN * K_RP / 1024;
+  static constexpr int K_INST = SD ? BN * K_HB / 1024 : BN * K_RP / 1024;
   static constexpr int R_INST = BN * R_RP / 1024;
   static constexpr int V_INST = BN * V_RB / 1024;
   static constexpr int K_DMA = (K_INST + DW - 1) / DW;
@@ -144,12 +157,14 @@ struct MfmaCfg {
   static_assert(K_RB == 128 || K_RB == 256, "K rows of 128 or 256 bytes");
   static_assert(DR == 0 || R_RB == 128, "rope rows of 128 bytes");
   static_assert(V_RB == 128 || V_RB == 256, "V rows of 128 or 256 bytes");
-  static_assert(K_INST * 1024 == BN * K_RP && R_INST * 1024 == BN * R_RP &&
+  static_assert(K_INST * 1024 == (SD ? BN * K_HB : BN * K_RP) && R_INST * 1024 == BN * R_RP &&
                     V_INST * 1024 == BN * V_RB,
                 "regions are whole KiB");
   static_assert(V_DMA * DW == V_INST && V_DMA >= 1, "V DMA splits evenly over the waves");
   static_assert(N_OPS <= 15, "vmcnt immediates");
   static_assert(V_BASE % 256 == 0 && VSLOT % 256 == 0, "V rows keep 256-byte alignment");
+  static_assert(!SD || (SSLOT % 256 == 0 && BN * (K_HB / 16) == WAVES * kWave),
+                "SD: one 16-byte chunk of a staged block per thread");
   static_assert(WAVES * 32 * O_ROW <= LDS, "epilogue staging must fit in the rings");
   static_assert(LDS + 64 <= 160 * 1024, "LDS per workgroup");
 };
@@ -220,9 +235,16 @@ struct MfmaKernel {
   }
   // Wait for this wave's DMA down to N outstanding instructions, then the
   // workgroup barrier (no fence: the compiler would add a vmcnt(0) wait).
+  // SD: the block's decoded K rows are plain LDS writes, so the wait also
+  // covers this wave's LDS operations (lgkmcnt(0)).
   template <int N>
   static __device__ __forceinline__ void publish() {
-    wait_vm<N>();
+    if constexpr (C::SD) {
+      static_assert(N >= 0 && N < 16, "vmcnt immediate");
+      __builtin_amdgcn_s_waitcnt(0x0070 | N);
+    } else {
+      wait_vm<N>();
+    }
     asm volatile("s_barrier" ::: "memory");
   }
   // Raw buffer resource (stride 0) over [base, base + bytes) in SGPRs.
@@ -246,6 +268,14 @@ struct MfmaKernel {
     const int q = 64 * n + lane;
     const int row = q / UPR, chunk = q % UPR;
     return chunk == UPR - 1 ? 0x80000000u : (uint32_t)(row * row_stride + chunk * 16);
+  }
+  // Per-lane source offset of DMA instruction n of an unpadded K staging
+  // region (SD): lane i fills 16-byte unit 64n + i, i.e. chunk (64n + i) %
+  // (K_HB/16) of row (64n + i) / (K_HB/16).
+  static __device__ __forceinline__ uint32_t dma_s_lane_off(int n, int lane, int row_stride) {
+    constexpr int UPR = C::K_HB / 16;
+    const int q = 64 * n + lane;
+    return (uint32_t)((q / UPR) * row_stride + (q % UPR) * 16);
   }
   // Per-lane source offset of DMA instruction n of an unpadded, swizzled V
   // region: instruction n covers rows RPI*n .. RPI*n+RPI-1; lane i fills
@@ -274,7 +304,8 @@ struct MfmaKernel {
     const int Hkv = p.num_kv_heads;
 #pragma unroll
     for (int i = 0; i < C::K_DMA; ++i)
-      d.k[i] = dma_k_lane_off<C::K_RB>(wave + C::DW * i, lane, Hkv * C::K_RB);
+      d.k[i] = C::SD ? dma_s_lane_off(wave + C::DW * i, lane, Hkv * C::K_HB)
+                     : dma_k_lane_off<C::K_HB>(wave + C::DW * i, lane, Hkv * C::K_HB);
     if constexpr (C::R_DMA > 0) {
 #pragma unroll
       for (int i = 0; i < C::R_DMA; ++i)
@@ -305,7 +336,7 @@ struct MfmaKernel {
     const uint32_t Hkv = (uint32_t)p.num_kv_heads;
     const size_t row0 = (size_t)s0 * Hkv + (uint32_t)g;
     DmaSrc d;
-    d.k = static_cast<const char*>(p.k) + row0 * C::K_RB;
+    d.k = static_cast<const char*>(p.k) + row0 * C::K_HB;
     d.r = static_cast<const char*>(p.k_rope) + row0 * C::R_RB;
     d.ks = reinterpret_cast<const char*>(p.k_scale + row0);
     d.v = static_cast<const char*>(p.v) + row0 * C::V_RB;
@@ -346,11 +377,13 @@ struct MfmaKernel {
     }
     const int kb = kspan ? kblk : 0, vb = vspan ? vblk : 0;  // keep addresses in range
     BlockDma b;
-    b.k = block_rsrc<C::K_RB>(d.k, d, kb, kspan);
+    b.k = block_rsrc<C::K_HB>(d.k, d, kb, kspan);
     if constexpr (C::DR > 0) b.r = block_rsrc<C::R_RB>(d.r, d, kb, kspan);
     if constexpr (C::FP8) b.ks = block_rsrc<4>(d.ks, d, kb, kspan);
     b.v = block_rsrc<C::V_RB>(d.v, d, vb, vspan);
-    b.kdst = sbase + (uint32_t)(kblk % C::NKS) * C::KSLOT + 1024u * (uint32_t)wave;
+    b.kdst = (C::SD ? sbase + C::S_BASE + (uint32_t)(kblk % C::NSS) * C::SSLOT
+                    : sbase + (uint32_t)(kblk % C::NKS) * C::KSLOT) +
+             1024u * (uint32_t)wave;
     b.vdst = sbase + C::V_BASE + (uint32_t)(vblk & (C::NVS - 1)) * C::VSLOT +
              1024u * (uint32_t)wave;
     return b;
@@ -374,7 +407,7 @@ struct MfmaKernel {
       dma16(b.r, m0, d.r[I]);
     } else if constexpr (OP < C::K_DMA + C::R_DMA + C::KS_DMA) {
       // wave 0's run starts at its slot's k_scale area
-      dma4(b.ks, wave == 0 ? b.kdst + C::KS_OFF : junk, d.ks);
+      dma4(b.ks, wave == 0 ? b.kdst + (C::SD ? C::BN * C::K_HB : C::KS_OFF) : junk, d.ks);
     } else {
       constexpr int I = OP - C::K_DMA - C::R_DMA - C::KS_DMA;
       dma16(b.v, b.vdst + 1024u * C::DW * I, d.v[I]);
@@ -409,7 +442,7 @@ struct MfmaKernel {
   static __device__ __forceinline__ Lanes lanes_of(int lane) {
     const int lane32 = lane & 31, hf = lane >> 5;
     Lanes ln;
-    ln.k = lane32 * C::K_RP + (C::F8MMA ? 32 : C::FP8 ? 8 : 16) * hf;
+    ln.k = lane32 * C::K_RP + (C::F8MMA ? 32 : (C::FP8 && !C::SD) ? 8 : 16) * hf;
     ln.r = lane32 * C::R_RP + 16 * hf;
     const int grp = lane >> 4, s = lane & 15;
     const int k1 = 4 * (grp >> 1) + (s >> 2);  // key row of the first read (u = 0)
@@ -434,7 +467,7 @@ struct MfmaKernel {
     return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   }
   static __device__ __forceinline__ QFrag s_frag(uint32_t kt, uint32_t rt, int s) {
-    if constexpr (C::FP8 && !C::F8MMA) {
+    if constexpr (C::FP8 && !C::F8MMA && !C::SD) {
       // E4M3 rows at pitch K_RP: step s covers depth 16 s .. 16 s + 15, 8
       // bytes per lane half
       if (s < C::QK_STEPS) {
@@ -444,7 +477,7 @@ struct MfmaKernel {
       }
       return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
           lp(rt) + 32 * (s - C::QK_STEPS));
-    } else if constexpr (C::FP8) {
+    } else if constexpr (C::F8MMA) {
       const i32x4 a0 = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
           lp(kt) + 64 * s);
       const i32x4 a1 = *reinterpret_cast<const __attribute__((address_space(3))) i32x4*>(
@@ -488,6 +521,27 @@ struct MfmaKernel {
     const i16x4 r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a1 + 8 * C::V_RB));
     const i16x8 r = {r1[0], r1[1], r1[2], r1[3], r2[0], r2[1], r2[2], r2[3]};
     return __builtin_bit_cast(bf16x8, r);
+  }
+
+  // SD: the staged fp8 rows of block blk, decoded to bfloat16 into its K
+  // slot (rows at pitch K_RP, as the bf16 kernel stores them), and its
+  // k_scale copied there.  One 16-byte chunk (16 codes) per thread.
+  static __device__ __forceinline__ void decode_block(uint32_t sbase, int blk, int tid) {
+    typedef __attribute__((address_space(3))) i32x4 li32x4;
+    typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
+    const uint32_t src = sbase + C::S_BASE + (uint32_t)(blk % C::NSS) * C::SSLOT;
+    const uint32_t dst = sbase + (uint32_t)(blk % C::NKS) * C::KSLOT;
+    constexpr int CPR = C::K_HB / 16;  // staged chunks per row
+    const int row = tid / CPR, ch = tid % CPR;
+    const i32x4 x = *reinterpret_cast<const li32x4*>(lp(src + row * C::K_HB + ch * 16));
+    lchar* d = const_cast<lchar*>(lp(dst + row * C::K_RP + ch * 32));
+    *reinterpret_cast<lbf16x8*>(d) = dec8(i32x2{x[0], x[1]});
+    *reinterpret_cast<lbf16x8*>(d + 16) = dec8(i32x2{x[2], x[3]});
+    if (tid < C::BN / 4) {
+      const i32x4 k4 =
+          *reinterpret_cast<const li32x4*>(lp(src + C::BN * C::K_HB + 16 * tid));
+      *reinterpret_cast<li32x4*>(const_cast<lchar*>(lp(dst + C::KS_OFF + 16 * tid))) = k4;
+    }
   }
 
   // ------------------------------------------------------------ pieces
@@ -851,15 +905,21 @@ struct MfmaKernel {
         return block_dma<SPLIT>(dsrc, sbase, wave, t + C::KLEAD, t + 2);
       };
       if (grp == 0)
-        for (int t = jlo - C::KLEAD; t < jlo + (C::KLEAD == 3 ? -1 : 0); ++t)
+        for (int t = jlo - C::KLEAD; t < jlo + (C::KLEAD >= 3 ? -1 : 0); ++t)
           dma_ops<0, C::N_OPS>(blk(t), dl, junk, wave);
       wait_vm<0>();
       __syncthreads();
+      if constexpr (C::SD) {
+        // the first two blocks are decoded here, the third in block jlo
+        decode_block(sbase, jlo, tid);
+        decode_block(sbase, jlo + 1, tid);
+        __syncthreads();
+      }
       if (has_sub) {
         const uint32_t ks0 = sbase + (uint32_t)(jlo % C::NKS) * C::KSLOT;
         s_tile(opaque(ks0 + C::K_OFF + ln.k), opaque(ks0 + C::R_OFF + ln.r), qf, qr, w);
       }
-      if constexpr (C::KLEAD == 3)
+      if constexpr (C::KLEAD >= 3)
         if (grp == 0) dma_ops<0, C::N_OPS>(blk(jlo - 1), dl, junk, wave);
 
       // Per wave the sub-tiles run as alternating half-steps X_0 G_0 X_1
@@ -909,7 +969,7 @@ struct MfmaKernel {
       using Y = std::true_type;
       using N = std::false_type;
       auto publish_block = [&]() {
-        if constexpr (C::KLEAD == 3)
+        if constexpr (C::KLEAD >= 3)
           publish<C::N_OPS>();  // batch j may stay in flight
         else
           publish<C::V_DMA>();  // batch j's K part must be in too
@@ -920,6 +980,10 @@ struct MfmaKernel {
         constexpr int GRP = decltype(grpc)::value;
         BlockDma bd;
         if constexpr (GRP == 0) bd = blk(j);
+        // SD: block j + 2 (staged by batch j - 2, published at barrier j - 1)
+        // is decoded into the slot that block j - 1 freed; barrier j
+        // publishes it before block j + 1 first reads it
+        if constexpr (C::SD) decode_block(sbase, j + 2, tid);
         xh(grpc, chk, P0{}, 2 * j, j, bd);
         gh(chk, P1{}, P0{}, 2 * j, j, j);
         xh(grpc, chk, P1{}, 2 * j + 1, j, bd);
