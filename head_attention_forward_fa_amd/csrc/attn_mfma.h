@@ -38,7 +38,7 @@
 //         sigma*log2(e)*S; P = 2^(sigma*log2(e)*S - m) via v_exp_f32.  The
 //         correction of O and l (the per-row correction buffer of
 //         SM100AttentionSMem, Methods: correction_smem) is applied lazily,
-//         only when some row's max grows by more than 8 (a factor 256), so
+//         only when some row's max grows by more than 32 (a factor 2^32), so
 //         almost every sub-tile skips it; O and l always share the same stale
 //         m, so O / l and LSE = (m + log2 l) ln 2 are unchanged.
 //   O^T += V^T P^T on the matrix cores.  P^T is already in the B-operand
@@ -612,8 +612,12 @@ struct MfmaKernel {
       }
     }
     const float mx = half_max(x) * cq;
-    // lazy correction: only when some row's max grew by more than 8
-    if (wave_any(mx > w.m + 8.0f)) {
+    // lazy correction: only when some row's max grew by more than kLazy
+    // (log2 units).  Until then P <= 2^kLazy: bf16 P, the float32 row sums
+    // and O keep their relative precision at any such scale, and O / l and
+    // LSE = (m + log2 l) ln 2 do not depend on which m they share.
+    constexpr float kLazy = 32.f;
+    if (wave_any(mx > w.m + kLazy)) {
       const float m_new = fmaxf(w.m, mx);
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(w.m - m_new);
       w.l *= alpha;
