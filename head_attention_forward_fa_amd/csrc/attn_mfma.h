@@ -11,9 +11,11 @@
 // Staging.  K (+ K_rope, + the fp8 k_scale) and V of coming blocks are
 // copied HBM -> LDS by buffer_load ... lds: each lane moves 16 bytes straight
 // into LDS (lane i of an instruction lands at byte 16 i of a 1 KiB run), with
-// no register staging.  The K ring has 4 slots and the V ring 3, so block
-// j+3's K and block j+2's V are requested while block j is computed, two
-// blocks before they are needed; each wave spreads its few DMA instructions
+// no register staging.  The K ring has 4 slots (3 with a rope part) and the
+// V ring 4, so block j+3's K and block j+2's V are requested while block j
+// is computed, two blocks before they are needed (exact fp8 without rope:
+// the fp8 K rows are staged four blocks ahead and decoded to bf16 K slots
+// by the whole workgroup two blocks ahead); each wave spreads its few DMA instructions
 // over the matrix-core slots of the block's first step instead of issuing
 // them in one burst.  A block's buffer resource ends at the sequence's last
 // key, so rows past the end arrive as zeros.  K rows are stored at a pitch of
