@@ -66,8 +66,10 @@ COPY_PROBE_MIB = 1024
 
 
 # the sources that decide what the attention kernel and its scheduler do on
-# the device (the other entry points of the library do not)
-KERNEL_SOURCES = ("attn_bf16.hip", "attn_fp8.hip", "attn_mfma.h", "common.h", "sched.hip")
+# the device (kernels.h holds the queue chunk rule; the other entry points of
+# the library do not matter)
+KERNEL_SOURCES = ("attn_bf16.hip", "attn_fp8.hip", "attn_mfma.h", "common.h", "kernels.h",
+                  "sched.hip")
 
 
 def kernel_sources_sha256() -> str:

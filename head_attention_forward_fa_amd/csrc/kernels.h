@@ -27,7 +27,12 @@ hipError_t launch_prepass(const int32_t* cu, int batch, int num_heads, int num_k
 // Non-causal: one group (all its q-tiles cost the same; consecutive items of
 // one group share their K/V in the L2, measured 6-8% faster than
 // interleaving the groups).
-inline int prepass_chunk(int causal) { return causal ? 8 : 1; }
+// causal: 8 groups per chunk for MHA; with GQA a group holds `group` query
+// heads' items, so the chunk shrinks to keep about as many items per chunk
+// (ragged GQA causal, Hq 32 / Hkv 8: +1.4%).
+inline int prepass_chunk(int causal, int group) {
+  return causal ? (group >= 8 ? 1 : 8 / group) : 1;
+}
 
 hipError_t launch_sched_visit(int batch, int num_heads, int tiles, const i32x4* table,
                               SchedState* st, int* visits, int grid,
