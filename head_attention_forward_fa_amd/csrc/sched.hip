@@ -19,8 +19,9 @@
 //     A queue runs chunk by chunk (a chunk: consecutive groups), a chunk in
 //     rounds: round k holds the k-th longest q-tile of each of its groups
 //     (causal cost grows with the tile index).  Causal: chunks of 8
-//     groups, so each chunk, and the queue, drains with short items and the
-//     CUs finish close together.  Non-causal: one group per chunk (equal
+//     groups (8 / query heads per KV head with GQA, so that a chunk holds
+//     about as many items), so each chunk, and the queue, drains with short
+//     items and the CUs finish close together.  Non-causal: one group per chunk (equal
 //     costs; a group's items share their K/V in the XCD's L2).
 //   * the attention kernel is launched with about (CUs x resident
 //     workgroups) workgroups; each pops items from queue blockIdx % 8 with
