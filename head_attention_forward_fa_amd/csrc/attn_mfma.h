@@ -36,13 +36,15 @@
 //         SM100AttentionSMem, Methods q_scale_smem, k_scale_smem).
 //   mask: only the wave's last sub-tile can cross the causal diagonal or the
 //         sequence end (sub-tiles and wave rows are both 32-aligned).
-//   online softmax in the log2 domain: m is the running row max of
+//   online softmax in the log2 domain: m is a running row max of
 //         sigma*log2(e)*S; P = 2^(sigma*log2(e)*S - m) via v_exp_f32.  The
 //         correction of O and l (the per-row correction buffer of
-//         SM100AttentionSMem, Methods: correction_smem) is applied lazily,
-//         only when some row's max grows by more than 32 (a factor 2^32), so
-//         almost every sub-tile skips it; O and l always share the same stale
-//         m, so O / l and LSE = (m + log2 l) ln 2 are unchanged.
+//         SM100AttentionSMem, Methods: correction_smem) is applied lazily:
+//         P is computed against the current m, and only when a lane's sum of
+//         P exceeds 2^32 (or at an item's first sub-tile) is the row max
+//         taken, O and l corrected and P recomputed, so almost every
+//         sub-tile spends no vector work on maxima; O and l always share the
+//         same stale m, so O / l and LSE = (m + log2 l) ln 2 are unchanged.
 //   O^T += V^T P^T on the matrix cores.  P^T is already in the B-operand
 //         layout (lane = query, 8 k-slots), so it goes from the S registers to
 //         the PV product with one v_cvt_pk_bf16_f32 per pair.  V stays
@@ -578,48 +580,113 @@ struct MfmaKernel {
     }
   }
 
+  // Exponentials of a sub-tile's scores against the running max m (S in
+  // w.st, left unchanged): P = 2^(cq S - m) packed as bf16 pairs into w.pw;
+  // returns this lane's float32 sum of the unrounded P.
+  static __device__ __forceinline__ float exp_pack(State& w, float cq, float m) {
+    float ls[2];
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const float p0 = fast_exp2(fmaf(w.st[e], cq, -m));
+      const float p1 = fast_exp2(fmaf(w.st[e + 1], cq, -m));
+      ls[0] = e == 0 ? p0 : ls[0] + p0;  // no add of the zero start
+      ls[1] = e == 0 ? p1 : ls[1] + p1;
+      w.pw[e >> 1] = pack_bf16x2(p0, p1);
+    }
+    // (two sum chains, and computed even when the caller will redo them:
+    // no branch around the common path)
+    asm volatile("" : "+v"(ls[0]), "+v"(ls[1]), "+v"(w.pw[0]), "+v"(w.pw[1]), "+v"(w.pw[2]),
+                 "+v"(w.pw[3]), "+v"(w.pw[4]), "+v"(w.pw[5]), "+v"(w.pw[6]), "+v"(w.pw[7]));
+    return ls[0] + ls[1];
+  }
+
   // Softmax half-step of a sub-tile whose S is in w.st: fp8 k_scale, the mask
   // when it is the wave's last sub-tile (keys past `rel` in lane-relative
-  // numbering hidden), row max, lazy correction of O and l, exponentials,
-  // row sums and the bf16 packing of P into w.pw.  Element e of a lane is key
-  // 8(e/4) + 4 hf + e%4 of the sub-tile.
+  // numbering hidden), exponentials, row sums and the bf16 packing of P into
+  // w.pw.  Element e of a lane is key 8(e/4) + 4 hf + e%4 of the sub-tile.
+  //
+  // The running max is lazy (the per-row correction buffer of
+  // SM100AttentionSMem, Methods: correction_smem, applied rarely): P is
+  // computed against the current m first, and only when a lane's sum of P
+  // exceeds 2^kLazy (so some P may exceed 2^(kLazy - 4), or be infinite),
+  // or at the item's first sub-tile (`first`, no max yet), is the row max
+  // taken, O and l corrected and P recomputed.  Otherwise
+  // every P <= 2^kLazy: bf16 P, the float32 row sums and O keep their
+  // relative precision at any such scale, and O / l and LSE = (m + log2 l)
+  // ln 2 do not depend on which m they share.  This spends no vector work on
+  // row maxima in the common case.
   template <int OP0, int OP1, bool MAYMASK>
-  static __device__ __forceinline__ void xphase(State& w, const float* ks, int hf, float cq_in,
-                                                float crope, bool mask, int rel,
+  static __device__ __forceinline__ void xphase(State& w, bool first, const float* ks, int hf,
+                                                float cq_in, float crope, bool mask, int rel,
                                                 const BlockDma& bd, const DmaLanes& dl,
                                                 uint32_t junk, int wave) {
     MHA_SLOT_FENCE();
     // this half-step's share of the block's DMA ops
     dma_ops<OP0, OP1>(bd, dl, junk, wave);
-    float x = -INFINITY;
     // mixed layout: the score goes straight to the log2 domain here
     // (q_scale k_scale S_nope and S_rope at their own multipliers); the
     // rest of the half-step then runs with multiplier 1
     const float cq = C::MIXED ? 1.f : cq_in;
     (void)crope;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if constexpr (C::MIXED)
-        w.st[e] = fmaf(w.st[e] * ks[8 * (e >> 2) + 4 * hf + (e & 3)], cq_in, w.sr[e] * crope);
-      else if constexpr (C::FP8)
-        w.st[e] *= ks[8 * (e >> 2) + 4 * hf + (e & 3)];
-      x = fmaxf(x, w.st[e]);
-    }
-    if (MAYMASK && mask) {
-      x = -INFINITY;
+    if constexpr (C::MIXED || C::FP8) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        if (8 * (e >> 2) + (e & 3) > rel) w.st[e] = -INFINITY;
-        x = fmaxf(x, w.st[e]);
+        if constexpr (C::MIXED)
+          w.st[e] = fmaf(w.st[e] * ks[8 * (e >> 2) + 4 * hf + (e & 3)], cq_in, w.sr[e] * crope);
+        else
+          w.st[e] *= ks[8 * (e >> 2) + 4 * hf + (e & 3)];
       }
     }
-    const float mx = half_max(x) * cq;
-    // lazy correction: only when some row's max grew by more than kLazy
-    // (log2 units).  Until then P <= 2^kLazy: bf16 P, the float32 row sums
-    // and O keep their relative precision at any such scale, and O / l and
-    // LSE = (m + log2 l) ln 2 do not depend on which m they share.
-    constexpr float kLazy = 32.f;
-    if (wave_any(mx > w.m + kLazy)) {
+    if constexpr (C::FP8) {
+      // fp8 layouts: row max first (their half-step is longer anyway, and
+      // the max-first form measured faster there)
+      float x = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (MAYMASK && mask && 8 * (e >> 2) + (e & 3) > rel) w.st[e] = -INFINITY;
+        x = fmaxf(x, w.st[e]);
+      }
+      const float mx = half_max(x) * cq;
+      constexpr float kLazy = 32.f;
+      if (wave_any(mx > w.m + kLazy)) {
+        const float m_new = fmaxf(w.m, mx);
+        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(w.m - m_new);
+        w.l *= alpha;
+#pragma unroll
+        for (int t = 0; t < C::DV_TILES; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) w.o[t][r] *= alpha;
+        w.m = m_new;
+      }
+      const float m_use = w.m == -INFINITY ? 0.f : w.m;
+      float ls[2];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        w.st[e] = fast_exp2(fmaf(w.st[e], cq, -m_use));
+        ls[e & 1] = e < 2 ? w.st[e] : ls[e & 1] + w.st[e];  // no add of the zero start
+        if (e & 1) w.pw[e >> 1] = pack_bf16x2(w.st[e - 1], w.st[e]);
+      }
+      w.l += ls[0] + ls[1];
+      (void)first;
+      MHA_SLOT_FENCE();
+      return;
+    }
+    if (MAYMASK && mask) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (8 * (e >> 2) + (e & 3) > rel) w.st[e] = -INFINITY;
+    }
+    constexpr float kLazyMax = 4294967296.f;  // 2^kLazy, kLazy = 32 (log2 units)
+    float ls = exp_pack(w, cq, w.m);
+    // (checked half-steps: also any row still without a visible key, whose
+    // m = -inf gives no usable P)
+    const bool big =
+        wave_any(ls > kLazyMax) | first | (MAYMASK && wave_any(w.m == -INFINITY));
+    if (big) {
+      float x = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x = fmaxf(x, w.st[e]);
+      const float mx = half_max(x) * cq;
       const float m_new = fmaxf(w.m, mx);
       const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(w.m - m_new);
       w.l *= alpha;
@@ -628,16 +695,10 @@ struct MfmaKernel {
 #pragma unroll
         for (int r = 0; r < 16; ++r) w.o[t][r] *= alpha;
       w.m = m_new;
+      // rows with no visible key yet keep m = -inf, P = 0
+      ls = exp_pack(w, cq, m_new == -INFINITY ? 0.f : m_new);
     }
-    const float m_use = w.m == -INFINITY ? 0.f : w.m;
-    float ls[2];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      w.st[e] = fast_exp2(fmaf(w.st[e], cq, -m_use));
-      ls[e & 1] = e < 2 ? w.st[e] : ls[e & 1] + w.st[e];  // no add of the zero start
-      if (e & 1) w.pw[e >> 1] = pack_bf16x2(w.st[e - 1], w.st[e]);
-    }
-    w.l += ls[0] + ls[1];
+    w.l += ls;
     MHA_SLOT_FENCE();
   }
 
@@ -951,8 +1012,9 @@ struct MfmaKernel {
         const float* ks =
             reinterpret_cast<const float*>(smem + (j % C::NKS) * C::KSLOT + C::KS_OFF) + 32 * H;
         if (!CHK || i < n_sub)
-          xphase<O0, O1, CHK>(w, ks, hf, cq, p.scale_log2, SPLIT ? i == last_sub : i == n_sub - 1,
-                              lim - 32 * i - 4 * hf, bd, dl, junk, wave);
+          xphase<O0, O1, CHK>(w, i == 2 * jlo, ks, hf, cq, p.scale_log2,
+                              SPLIT ? i == last_sub : i == n_sub - 1, lim - 32 * i - 4 * hf, bd,
+                              dl, junk, wave);
         else
           dma_ops<O0, O1>(bd, dl, junk, wave);
       };
