@@ -63,7 +63,7 @@ def load() -> ctypes.CDLL:
     lib.mha_fwd_kernel_info.restype = ctypes.c_int
     lib.mha_fwd_set_kernel_events.argtypes = [vp, vp]
     lib.mha_fwd_set_kernel_events.restype = ctypes.c_int
-    lib.mha_sched_visit.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.mha_sched_visit.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.mha_sched_visit.restype = ctypes.c_int
     lib.mha_quantize_fp8.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp]
     lib.mha_quantize_fp8.restype = ctypes.c_int

@@ -220,6 +220,15 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   const bool fp8 = dtype == MHA_DTYPE_FP8_E4M3 || dtype == MHA_DTYPE_FP8_E4M3_FASTACC;
   if (fp8 != (q_scale != nullptr) || fp8 != (k_scale != nullptr))
     return fail(MHA_ERR_INVALID_ARG, "q_scale and k_scale must be given iff dtype is FP8_E4M3");
+  auto misaligned = [](const void* ptr, uintptr_t a) {
+    return reinterpret_cast<uintptr_t>(ptr) % a != 0;
+  };
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) ||
+      misaligned(q_rope, 16) || misaligned(k_rope, 16))
+    return fail(MHA_ERR_INVALID_ARG, "q, k, v, o, q_rope, k_rope must be 16-byte aligned");
+  if (misaligned(lse, 4) || misaligned(cu_seqlens, 4) || misaligned(q_scale, 4) ||
+      misaligned(k_scale, 4))
+    return fail(MHA_ERR_INVALID_ARG, "lse, cu_seqlens, q_scale, k_scale must be 4-byte aligned");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   int dev = 0;
@@ -264,8 +273,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   auto* scratch = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
 
   const int chunk = mha::prepass_chunk(causal, num_heads / num_kv_heads);
-  e = mha::launch_prepass(cu_seqlens, batch, num_heads, num_kv_heads, causal, var->block_m,
-                          var->block_n, num_splits, plan.capacity, chunk, table, st, scratch, s);
+  e = mha::launch_prepass(cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads, causal,
+                          var->block_m, var->block_n, num_splits, plan.capacity, chunk, table, st,
+                          scratch, s);
   if (e != hipSuccess) return fail_hip(e, "scheduler prepass launch");
 
   mha::AttnParams p;
@@ -306,9 +316,10 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
     if (e != hipSuccess) return fail_hip(e, "hipEventRecord (stop)");
   }
   if (num_splits > 1) {
+    // (a refused call writes no partial; the merge then writes nothing)
     e = mha::launch_combine(o_part, lse_part, num_splits, total_tokens,
                             split_here ? cu_seqlens + batch : nullptr, num_heads, v_dim,
-                            dtype != MHA_DTYPE_F32, o, lse, s);
+                            dtype != MHA_DTYPE_F32, o, lse, st, s);
     if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
   }
   return MHA_OK;
@@ -372,7 +383,7 @@ int mha_combine_splits(const float* o_partial, const float* lse_partial, int32_t
     return fail(MHA_ERR_INVALID_ARG, "o_partial and o must be 16-byte aligned");
   hipError_t e = mha::launch_combine(o_partial, lse_partial, num_splits, total_tokens, nullptr,
                                      num_heads, v_dim, out_dtype == MHA_DTYPE_BF16, o, lse,
-                                     static_cast<hipStream_t>(stream));
+                                     nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
   return MHA_OK;
 }
@@ -405,10 +416,11 @@ int mha_fwd_kernel_info(int32_t dtype, int32_t head_dim_nope, int32_t head_dim_r
 
 int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
                     int32_t num_heads, int32_t num_kv_heads, int32_t causal, int32_t block_m,
-                    int32_t grid, int32_t* visits, void* stream) {
+                    int32_t grid, int32_t protocol, int32_t* visits, void* stream) {
   g_err.clear();
   int rc = check_scalars(batch, max_seqlen, num_heads, num_kv_heads);
   if (rc) return rc;
+  if (protocol != 0 && protocol != 1) return fail(MHA_ERR_INVALID_ARG, "protocol must be 0 or 1");
   if (!cu_seqlens) return fail(MHA_ERR_INVALID_ARG, "cu_seqlens is NULL");
   if (!visits) return fail(MHA_ERR_INVALID_ARG, "visits is NULL");
   if (causal != 0 && causal != 1) return fail(MHA_ERR_INVALID_ARG, "causal must be 0 or 1");
@@ -435,12 +447,12 @@ int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen
   auto* table = reinterpret_cast<mha::i32x4*>(ws + kStateBytes);
   auto* scratch = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
   const int chunk = mha::prepass_chunk(causal, num_heads / num_kv_heads);
-  e = mha::launch_prepass(cu_seqlens, batch, num_heads, num_kv_heads, causal, block_m, block_n,
-                          1, plan.capacity, chunk, table, st, scratch, s);
+  e = mha::launch_prepass(cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads, causal, block_m,
+                          block_n, 1, plan.capacity, chunk, table, st, scratch, s);
   if (e != hipSuccess) return fail_hip(e, "scheduler prepass launch");
   if (grid == 0) grid = cu_count(dev) * 2;
   const int tiles = (int)(((long long)max_seqlen + block_m - 1) / block_m);
-  e = mha::launch_sched_visit(batch, num_heads, tiles, table, st, visits, grid, s);
+  e = mha::launch_sched_visit(batch, num_heads, tiles, protocol, table, st, visits, grid, s);
   if (e != hipSuccess) return fail_hip(e, "visit kernel launch");
   return MHA_OK;
 }

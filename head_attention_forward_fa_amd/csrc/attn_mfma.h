@@ -680,8 +680,9 @@ struct MfmaKernel {
     float ls = exp_pack(w, cq, w.m);
     // (checked half-steps: also any row still without a visible key, whose
     // m = -inf gives no usable P)
-    const bool big =
-        wave_any(ls > kLazyMax) | first | (MAYMASK && wave_any(w.m == -INFINITY));
+    // (bitwise or: every term is evaluated, no branch around the check)
+    const bool big = (int)wave_any(ls > kLazyMax) | (int)first |
+                     (int)(MAYMASK && wave_any(w.m == -INFINITY));
     if (big) {
       float x = -INFINITY;
 #pragma unroll

@@ -29,11 +29,15 @@ namespace {
 constexpr int kCombineThreads = 256;
 
 // T: tokens of the partials' layout; t_out (device, may be null): tokens of
-// the output when fewer (the rest of the partial rows are not merged), else T
+// the output when fewer (the rest of the partial rows are not merged), else T;
+// sched (may be null): the scheduler state of the split attention call, whose
+// refusal (status != 0: no partial was written) leaves o and lse untouched
 template <int DV, bool BF16>
 __global__ __launch_bounds__(kCombineThreads) void combine_splits_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part, int num_splits, int T,
-    const int32_t* __restrict__ t_out, int H, void* __restrict__ o, float* __restrict__ lse) {
+    const int32_t* __restrict__ t_out, int H, void* __restrict__ o, float* __restrict__ lse,
+    const SchedState* __restrict__ sched) {
+  if (sched && sched->status != 0) return;
   constexpr int LPR = DV / 4;  // lanes per row
   constexpr int RPB = kCombineThreads / LPR;
   const int c = threadIdx.x % LPR;
@@ -75,13 +79,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_splits_kernel(
 
 template <int DV, bool BF16>
 hipError_t launch_dv(const float* o_part, const float* lse_part, int num_splits, int T,
-                     const int32_t* t_out, int H, void* o, float* lse, hipStream_t stream) {
+                     const int32_t* t_out, int H, void* o, float* lse, const SchedState* sched,
+                     hipStream_t stream) {
   constexpr int RPB = kCombineThreads / (DV / 4);
   const long long rows = (long long)T * H;
   const long long blocks = (rows + RPB - 1) / RPB;
   hipLaunchKernelGGL((combine_splits_kernel<DV, BF16>), dim3((unsigned)blocks),
                      dim3(kCombineThreads), 0, stream, o_part, lse_part, num_splits, T, t_out, H,
-                     o, lse);
+                     o, lse, sched);
   return hipGetLastError();
 }
 
@@ -89,15 +94,17 @@ hipError_t launch_dv(const float* o_part, const float* lse_part, int num_splits,
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, int num_splits, int T,
                           const int32_t* t_out, int H, int dv, bool bf16_out, void* o, float* lse,
-                          hipStream_t stream) {
+                          const SchedState* sched, hipStream_t stream) {
   if (dv == 64)
-    return bf16_out ? launch_dv<64, true>(o_part, lse_part, num_splits, T, t_out, H, o, lse, stream)
+    return bf16_out ? launch_dv<64, true>(o_part, lse_part, num_splits, T, t_out, H, o, lse,
+                                          sched, stream)
                     : launch_dv<64, false>(o_part, lse_part, num_splits, T, t_out, H, o, lse,
-                                           stream);
+                                           sched, stream);
   if (dv == 128)
-    return bf16_out
-               ? launch_dv<128, true>(o_part, lse_part, num_splits, T, t_out, H, o, lse, stream)
-               : launch_dv<128, false>(o_part, lse_part, num_splits, T, t_out, H, o, lse, stream);
+    return bf16_out ? launch_dv<128, true>(o_part, lse_part, num_splits, T, t_out, H, o, lse,
+                                           sched, stream)
+                    : launch_dv<128, false>(o_part, lse_part, num_splits, T, t_out, H, o, lse,
+                                            sched, stream);
   return hipErrorInvalidValue;
 }
 

@@ -16,9 +16,12 @@ constexpr int kBlockM_F32 = 64;
 constexpr int kBlockN_F32 = 32;
 
 // chunk: groups per chunk of a queue (>= 1), see prepass_chunk.
-hipError_t launch_prepass(const int32_t* cu, int batch, int num_heads, int num_kv_heads,
-                          int causal, int bm, int bn, int num_splits, int capacity, int chunk,
-                          i32x4* table, SchedState* st, int* scratch, hipStream_t stream);
+// Refuses (status 1, empty queues) when a length is negative or above
+// max_seqlen, or when the items exceed `capacity`.
+hipError_t launch_prepass(const int32_t* cu, int batch, int max_seqlen, int num_heads,
+                          int num_kv_heads, int causal, int bm, int bn, int num_splits,
+                          int capacity, int chunk, i32x4* table, SchedState* st, int* scratch,
+                          hipStream_t stream);
 
 // Groups per queue chunk.  Causal: 8 groups (their longest q-tiles first:
 // the CUs then finish close together; measured against the whole queue as
@@ -34,8 +37,10 @@ inline int prepass_chunk(int causal, int group) {
   return causal ? (group >= 8 ? 1 : 8 / group) : 1;
 }
 
-hipError_t launch_sched_visit(int batch, int num_heads, int tiles, const i32x4* table,
-                              SchedState* st, int* visits, int grid,
+// protocol: 0 take(), 1 reserve() / resolve() placed as the attention kernel
+// places them (see sched_visit_kernel)
+hipError_t launch_sched_visit(int batch, int num_heads, int tiles, int protocol,
+                              const i32x4* table, SchedState* st, int* visits, int grid,
                               hipStream_t stream);
 
 // Per-row fp8 quantisation (quant.hip): rows x cols input (bf16 bits or
@@ -45,9 +50,10 @@ hipError_t launch_fp8_quant(const void* x, bool bf16, int64_t rows, int cols, ui
 
 // Split-KV merge (combine.hip): o_part [num_splits, T, H, Dv] float32 and
 // lse_part [num_splits, H, T] -> o [T, H, Dv] (bf16 or float32), lse [H, T].
+// With `sched` set, nothing is written when the prepass refused the call.
 hipError_t launch_combine(const float* o_part, const float* lse_part, int num_splits, int T,
                           const int32_t* t_out, int H, int dv, bool bf16_out, void* o, float* lse,
-                          hipStream_t stream);
+                          const SchedState* sched, hipStream_t stream);
 
 // A kernel variant: its launcher and its occupancy (resident workgroups per
 // CU at its LDS and register footprint, computed once per device).

@@ -29,6 +29,8 @@
 //
 // Cost of an item, in BN-key blocks: causal ceil(min(L, (qt+1)*BM) / BN),
 // non-causal ceil(L / BN).
+#include <climits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -58,9 +60,9 @@ __device__ __forceinline__ int queue_rank(int x, int j) {
 }
 
 __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
-    const int32_t* __restrict__ cu, int batch, int num_heads, int num_kv_heads, int causal,
-    int bm, int bn, int num_splits, int capacity, int chunk, i32x4* __restrict__ table,
-    SchedState* __restrict__ st, int* __restrict__ scratch) {
+    const int32_t* __restrict__ cu, int batch, int max_seqlen, int num_heads, int num_kv_heads,
+    int causal, int bm, int bn, int num_splits, int capacity, int chunk,
+    i32x4* __restrict__ table, SchedState* __restrict__ st, int* __restrict__ scratch) {
   __shared__ long long s_cost[kSortedMax];
   __shared__ int s_items[kSortedMax];   // group -> item count
   __shared__ int s_irank[kSortedMax];   // rank -> item count
@@ -79,16 +81,20 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
   __syncthreads();
 
   // A: per-group cost and item count; the item total by a block reduction
-  // (in 64 bits: garbage lengths must not wrap past the capacity check)
+  // (in 64 bits: garbage lengths must not wrap past the capacity check).  A
+  // length above max_seqlen refuses the call: the split-KV partials are laid
+  // out for batch x max_seqlen tokens.
   long long my_items = 0;
   int my_rmax = 0;  // most q-tiles of a group
   for (int i = tid; i < n; i += kPrepassThreads) {
     const int b = i / num_kv_heads;
     const int L = cu[b + 1] - cu[b];
     const int nqt = L > 0 ? (L + bm - 1) / bm : 0;
-    if (L < 0 || nqt >= kMaxQTilesPerSeq) s_bad = 1;
-    const int items = nqt * group * num_splits;
-    my_items += items;
+    if (L < 0 || L > max_seqlen || nqt >= kMaxQTilesPerSeq) s_bad = 1;
+    const long long items64 = (long long)nqt * group * num_splits;
+    // (stored as int only for use after the capacity check, where it fits)
+    const int items = (int)min(items64, (long long)INT_MAX);
+    my_items += items64;
     my_rmax = max(my_rmax, nqt);
     if (sorted) {
       s_cost[i] = group_cost(L, bm, bn, causal) * group;
@@ -312,7 +318,14 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
   }
 }
 
+// protocol 0: take() (the next item reserved when the current one starts);
+// protocol 1: reserve() and resolve() as two steps at the places the
+// attention kernel uses them: an item of nb key blocks (here nb = qt % 5, so
+// that items with no blocks occur too) reserves at block max(0, nb - 3) and
+// reads the entry at block max(0, nb - 1), with a workgroup barrier per block;
+// an item with no blocks does both after its (empty) block loop.
 __global__ __launch_bounds__(256) void sched_visit_kernel(int batch, int num_heads, int tiles,
+                                                           int protocol,
                                                            const i32x4* __restrict__ table,
                                                            SchedState* __restrict__ st,
                                                            int* __restrict__ visits) {
@@ -321,41 +334,58 @@ __global__ __launch_bounds__(256) void sched_visit_kernel(int batch, int num_hea
   const bool w0 = threadIdx.x < kWave;
   if (w0) {
     fetch.init(st);
-    const i32x4 e0 = fetch.take(st, table);
+    const i32x4 e0 = protocol ? fetch.resolve(st, table) : fetch.take(st, table);
     if (threadIdx.x == 0) s_item[0] = e0;
   }
   for (int it = 0;; ++it) {
     __syncthreads();
     const i32x4 e = s_item[it & 1];
     if (e[1] < 0) break;
-    if (w0) {
-      const i32x4 nxt = fetch.take(st, table);
-      if (threadIdx.x == 0) {
-        s_item[(it + 1) & 1] = nxt;
-        const WorkItem w = decode_item(e);
-        if (w.b < batch && w.h < num_heads && w.qt < tiles)
-          atomicAdd(&visits[(w.h * batch + w.b) * tiles + w.qt], 1);
+    const WorkItem w = decode_item(e);
+    i32x4 nxt = {0, -1, 0, 0};
+    if (protocol == 0) {
+      if (w0) nxt = fetch.take(st, table);
+    } else {
+      const int nb = w.qt % 5;
+      const int j_res = max(0, nb - 3), j_get = max(0, nb - 1);
+      for (int j = 0; j < nb; ++j) {
+        if (w0) {
+          if (j == j_res) fetch.reserve(st);
+          if (j == j_get) nxt = fetch.resolve(st, table);
+        }
+        __syncthreads();
       }
+      if (w0 && nb <= 0) {
+        fetch.reserve(st);
+        nxt = fetch.resolve(st, table);
+      }
+    }
+    if (threadIdx.x == 0) {
+      s_item[(it + 1) & 1] = nxt;
+      if (w.b < batch && w.h < num_heads && w.qt < tiles)
+        atomicAdd(&visits[(w.h * batch + w.b) * tiles + w.qt], 1);
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_prepass(const int32_t* cu, int batch, int num_heads, int num_kv_heads,
-                          int causal, int bm, int bn, int num_splits, int capacity, int chunk,
-                          i32x4* table, SchedState* st, int* scratch, hipStream_t stream) {
+hipError_t launch_prepass(const int32_t* cu, int batch, int max_seqlen, int num_heads,
+                          int num_kv_heads, int causal, int bm, int bn, int num_splits,
+                          int capacity, int chunk, i32x4* table, SchedState* st, int* scratch,
+                          hipStream_t stream) {
   if (chunk < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(sched_prepass_kernel, dim3(1), dim3(kPrepassThreads), 0, stream, cu, batch,
-                     num_heads, num_kv_heads, causal, bm, bn, num_splits, capacity, chunk, table,
-                     st, scratch);
+                     max_seqlen, num_heads, num_kv_heads, causal, bm, bn, num_splits, capacity,
+                     chunk, table, st, scratch);
   return hipGetLastError();
 }
 
-hipError_t launch_sched_visit(int batch, int num_heads, int tiles, const i32x4* table,
-                              SchedState* st, int* visits, int grid, hipStream_t stream) {
+hipError_t launch_sched_visit(int batch, int num_heads, int tiles, int protocol,
+                              const i32x4* table, SchedState* st, int* visits, int grid,
+                              hipStream_t stream) {
   hipLaunchKernelGGL(sched_visit_kernel, dim3(grid), dim3(256), 0, stream, batch, num_heads,
-                     tiles, table, st, visits);
+                     tiles, protocol, table, st, visits);
   return hipGetLastError();
 }
 

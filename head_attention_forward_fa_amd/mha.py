@@ -162,8 +162,10 @@ def mha_fwd_kernel_info(dtype_code: int, head_dim_nope: int, head_dim_rope: int,
 
 def mha_sched_visit(cu_seqlens: torch.Tensor, max_seqlen: int, num_heads: int,
                     num_kv_heads: int, causal: bool, block_m: int = 256,
-                    grid: int = 0) -> torch.Tensor:
-    """Runs the scheduler alone; returns visit counts [Hq, B, tiles] (int32)."""
+                    grid: int = 0, protocol: int = 1) -> torch.Tensor:
+    """Runs the scheduler alone; returns visit counts [Hq, B, tiles] (int32).
+    protocol 0: next item fetched when an item starts; 1: reserved and read
+    near the end of an item, as the matrix-core kernel does."""
     B = cu_seqlens.numel() - 1
     tiles = (max_seqlen + block_m - 1) // block_m
     visits = torch.zeros((num_heads, B, max(tiles, 1)), dtype=torch.int32,
@@ -172,7 +174,8 @@ def mha_sched_visit(cu_seqlens: torch.Tensor, max_seqlen: int, num_heads: int,
     with torch.cuda.device(cu_seqlens.device):
         st = nat.load().mha_sched_visit(_ptr(cu_seqlens), int(B), int(max_seqlen),
                                         int(num_heads), int(num_kv_heads), int(bool(causal)),
-                                        int(block_m), int(grid), _ptr(visits), stream)
+                                        int(block_m), int(grid), int(protocol), _ptr(visits),
+                                        stream)
     nat.check(st)
     return visits
 

@@ -88,10 +88,10 @@ typedef enum {
  *               for float32 and 256 for bf16 / fp8).  0 means every
  *               sequence is empty: the scalar arguments are still checked,
  *               but nothing is read, written or launched and the tensor
- *               pointers may be NULL.  When the lengths
- *               break this bound so far that the work items would not fit in
- *               that table, the device refuses the whole call and writes
- *               nothing.
+ *               pointers may be NULL.  When a length breaks this bound, the
+ *               device refuses the whole call and writes nothing (O and LSE
+ *               keep what they held; the status is only visible on the
+ *               device, as the lengths are not read on the host).
  *   num_heads, num_kv_heads   query and key/value heads; num_heads must be a
  *               multiple of num_kv_heads
  *   head_dim_nope, head_dim_rope, v_dim   Dn, Dr (0 = no rope part), Dv
@@ -112,6 +112,11 @@ typedef enum {
  *               k_scale_smem).  Required iff dtype is FP8_E4M3 or
  *               FP8_E4M3_FASTACC, else NULL.
  *   stream      hipStream_t or NULL
+ *
+ * Alignment: q, k, v, o, q_rope and k_rope must be 16-byte aligned (the
+ * kernels move them in 16-byte units), lse, cu_seqlens, q_scale and k_scale
+ * 4-byte aligned; MHA_ERR_INVALID_ARG otherwise (checked on the host, before
+ * any HIP call).
  *
  * Compiled set (MHA_ERR_UNSUPPORTED otherwise):
  *   F32      (Dn, Dr, Dv) in {(64,0,64), (128,0,128), (128,64,128)}
@@ -186,12 +191,18 @@ int mha_fwd_set_kernel_events(void* start_event, void* stop_event);
  * visits[h * (batch * tiles) + b * tiles + qtile], tiles =
  * ceil(max_seqlen / block_m).  visits is a caller-owned device int32 array of
  * num_heads * batch * tiles entries, zeroed by the caller.  block_m is 64 or
- * 256 (the float32 and MFMA kernels' query tiles).  Every existing item must
- * end with exactly one visit.
+ * 256 (the float32 and MFMA kernels' query tiles).  protocol 0 fetches the
+ * next item when the current one starts (as the float32 kernel does);
+ * protocol 1 reserves it and reads its entry as two separate steps near the
+ * end of the current item, with workgroup barriers in between (as the
+ * matrix-core kernel does; items with no key blocks included).  Every
+ * existing item must end with exactly one visit.  MHA_ERR_INVALID_ARG for a
+ * protocol other than 0 or 1.
  */
 int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
                     int32_t num_heads, int32_t num_kv_heads, int32_t causal,
-                    int32_t block_m, int32_t grid, int32_t* visits, void* stream);
+                    int32_t block_m, int32_t grid, int32_t protocol, int32_t* visits,
+                    void* stream);
 
 /*
  * mha_fwd_splitkv -- mha_fwd with the keys of every query tile cut into

@@ -180,6 +180,11 @@ EXTRA_WORKLOADS = {
     "bf16_causal_b1_h4_s16384_d128": dict(
         dtype="bf16", seqlens=[16384], num_heads=4, num_kv_heads=4,
         head_dim_nope=128, v_dim=128, causal=True),
+    # the headline shape without the causal mask (the non-causal queue layout
+    # and every query tile at full key length)
+    "bf16_noncausal_b4_h32_s4096_d128": dict(
+        dtype="bf16", seqlens=[4096] * 4, num_heads=32, num_kv_heads=32,
+        head_dim_nope=128, v_dim=128, causal=False),
 }
 
 

@@ -60,6 +60,12 @@ BAD = [
     dict(dtype=nat.MHA_DTYPE_FP8_E4M3_FASTACC, k_scale=FAKE),
     dict(q_scale=FAKE, k_scale=FAKE),             # scales with bf16
     dict(scale=math.nan), dict(scale=math.inf),
+    # alignment: 16 bytes for the tensors moved in 16-byte units, 4 for the rest
+    dict(q=FAKE + 2), dict(k=FAKE + 8), dict(v=FAKE + 4), dict(o=FAKE + 2),
+    dict(dr=64, q_rope=FAKE + 8, k_rope=FAKE), dict(dr=64, q_rope=FAKE, k_rope=FAKE + 2),
+    dict(lse=FAKE + 2), dict(cu=FAKE + 1),
+    dict(dtype=nat.MHA_DTYPE_FP8_E4M3, q_scale=FAKE + 2, k_scale=FAKE),
+    dict(dtype=nat.MHA_DTYPE_FP8_E4M3, q_scale=FAKE, k_scale=FAKE + 1),
 ]
 
 
@@ -101,11 +107,14 @@ def test_supported_set():
 def test_sched_visit_validation():
     lib = nat.load()
     for bad_block_m in (32, 128):
-        assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, bad_block_m, 0, FAKE,
+        assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, bad_block_m, 0, 1, FAKE,
                                    None) == nat.MHA_ERR_INVALID_ARG
-    assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 256, 0, None, None) == nat.MHA_ERR_INVALID_ARG
-    assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 256, -1, FAKE, None) == nat.MHA_ERR_INVALID_ARG
-    assert lib.mha_sched_visit(FAKE, 1, 0, 4, 2, 1, 256, 0, FAKE, None) == nat.MHA_OK
+    assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 256, 0, 1, None, None) == nat.MHA_ERR_INVALID_ARG
+    assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 256, -1, 1, FAKE, None) == nat.MHA_ERR_INVALID_ARG
+    for bad_protocol in (-1, 2):
+        assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 256, 0, bad_protocol, FAKE,
+                                   None) == nat.MHA_ERR_INVALID_ARG
+    assert lib.mha_sched_visit(FAKE, 1, 0, 4, 2, 1, 256, 0, 1, FAKE, None) == nat.MHA_OK
 
 
 def test_set_kernel_events_validation():

@@ -54,3 +54,25 @@ def test_auto_split_matches_oracle_and_stays_in_bounds(case):
     eo, el = max_abs(o64, ref_o), max_abs(l64, ref_lse)
     assert eo <= TOL_O[dt], f"O max-abs {eo}"
     assert el <= TOL_LSE, f"LSE max-abs {el}"
+
+
+@pytest.mark.parametrize("num_splits", [1, 3])  # 1: mha_fwd's own splits; 3: mha_fwd_splitkv
+def test_split_paths_refuse_lengths_above_max_seqlen_without_writes(num_splits):
+    """A length above max_seqlen makes the prepass refuse (the partials are
+    laid out for batch x max_seqlen tokens): no work item runs and the merge
+    writes nothing, so O and LSE keep what they held."""
+    from head_attention_forward_fa_amd import mha_fwd, mha_fwd_auto_splits
+    inp = mi.make_inputs(dtype="bf16", seqlens=[2048, 600], num_heads=2, num_kv_heads=2,
+                         head_dim_nope=128, v_dim=128, causal=True, seed=12)
+    short = 2000  # the first sequence is longer
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if num_splits == 1:
+        assert mha_fwd_auto_splits(2, short, 2, True, 128, cus) > 1, "meant to split by itself"
+    t = device_tensors(inp)
+    T = inp.total_tokens
+    o = torch.full((T, 2, 128), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    lse = torch.full((2, T), 7.0, dtype=torch.float32, device="cuda:0")
+    mha_fwd(t["q"], t["k"], t["v"], causal=True, cu_seqlens=t["cu_seqlens"], max_seqlen=short,
+            num_splits=num_splits, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((o == 7.0).all()) and bool((lse == 7.0).all())

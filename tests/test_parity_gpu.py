@@ -199,9 +199,13 @@ def test_overflowing_lengths_are_refused_without_writes():
     assert bool((out == 7.0).all()) and bool((lse == 7.0).all())
 
 
+# protocol 0: the next item fetched when an item starts (the float32 kernel);
+# protocol 1: reserved and read in two steps near the end of an item, items
+# with no key blocks included (the matrix-core kernel)
+@pytest.mark.parametrize("protocol", [0, 1])
 @pytest.mark.parametrize("block_m", [64, 256])
 @pytest.mark.parametrize("grid", [0, 1, 7, 1000])
-def test_scheduler_visits_every_item_once(block_m, grid):
+def test_scheduler_visits_every_item_once(block_m, grid, protocol):
     from head_attention_forward_fa_amd import mha_sched_visit
     rng = np.random.default_rng(block_m + grid)
     lens = rng.integers(0, 1500, size=23)
@@ -210,7 +214,8 @@ def test_scheduler_visits_every_item_once(block_m, grid):
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     hq, hkv = 8, 2
     mx = int(lens.max())
-    visits = mha_sched_visit(torch.from_numpy(cu).cuda(), mx, hq, hkv, True, block_m, grid)
+    visits = mha_sched_visit(torch.from_numpy(cu).cuda(), mx, hq, hkv, True, block_m, grid,
+                             protocol)
     torch.cuda.synchronize()
     tiles = (mx + block_m - 1) // block_m
     want = np.zeros((hq, len(lens), tiles), dtype=np.int32)
@@ -219,8 +224,9 @@ def test_scheduler_visits_every_item_once(block_m, grid):
     assert np.array_equal(visits.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("protocol", [0, 1])
 @pytest.mark.parametrize("causal", [False, True])
-def test_scheduler_many_groups_index_mode(causal):
+def test_scheduler_many_groups_index_mode(causal, protocol):
     # more (sequence, KV head) groups than the prepass ranks in LDS: the
     # contiguous-range queue assignment must still cover every item once
     from head_attention_forward_fa_amd import mha_sched_visit
@@ -229,7 +235,8 @@ def test_scheduler_many_groups_index_mode(causal):
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     hq, hkv = 8, 4
     mx = int(lens.max())
-    visits = mha_sched_visit(torch.from_numpy(cu).cuda(), mx, hq, hkv, causal, 256, 0)
+    visits = mha_sched_visit(torch.from_numpy(cu).cuda(), mx, hq, hkv, causal, 256, 0,
+                             protocol)
     torch.cuda.synchronize()
     tiles = (mx + 255) // 256
     want = np.zeros((hq, len(lens), tiles), dtype=np.int32)
@@ -238,10 +245,11 @@ def test_scheduler_many_groups_index_mode(causal):
     assert np.array_equal(visits.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("protocol", [0, 1])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("nseq,hkv,maxlen", [(511, 4, 2600), (256, 8, 2600), (9, 1, 2600),
                                             (300, 2, 600)])
-def test_scheduler_ranked_groups_cover_every_item_once(nseq, hkv, maxlen, causal):
+def test_scheduler_ranked_groups_cover_every_item_once(nseq, hkv, maxlen, causal, protocol):
     # groups ranked in LDS (up to 2048 of them, padded to a power of two for
     # the sort) and laid out chunk by chunk, round by round, in each queue
     # (short sequences: chunks of many groups)
@@ -252,7 +260,8 @@ def test_scheduler_ranked_groups_cover_every_item_once(nseq, hkv, maxlen, causal
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     hq = 2 * hkv
     mx = int(lens.max())
-    visits = mha_sched_visit(torch.from_numpy(cu).cuda(), mx, hq, hkv, causal, 256, 0)
+    visits = mha_sched_visit(torch.from_numpy(cu).cuda(), mx, hq, hkv, causal, 256, 0,
+                             protocol)
     torch.cuda.synchronize()
     tiles = (mx + 255) // 256
     want = np.zeros((hq, len(lens), tiles), dtype=np.int32)
