@@ -24,7 +24,7 @@ MHA_ERR_HIP = 3
 
 EXPORTS = ("mha_fwd", "mha_fwd_last_error", "mha_fwd_supported", "mha_fwd_kernel_info",
            "mha_fwd_set_kernel_events", "mha_sched_visit", "mha_quantize_fp8",
-           "mha_fwd_splitkv", "mha_combine_splits", "mha_fwd_auto_splits")
+           "mha_fwd_splitkv", "mha_combine_splits", "mha_fwd_auto_splits", "mha_fwd_noalloc")
 
 _lib = None
 
@@ -54,6 +54,8 @@ def load() -> ctypes.CDLL:
                             i32, f32, i32,             # causal softmax_scale dtype
                             vp, vp, vp]                # q_scale k_scale stream
     lib.mha_fwd.restype = ctypes.c_int
+    lib.mha_fwd_noalloc.argtypes = lib.mha_fwd.argtypes
+    lib.mha_fwd_noalloc.restype = ctypes.c_int
     lib.mha_fwd_last_error.argtypes = []
     lib.mha_fwd_last_error.restype = ctypes.c_char_p
     lib.mha_fwd_supported.argtypes = [i32, i32, i32, i32]

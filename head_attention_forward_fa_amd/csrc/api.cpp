@@ -60,6 +60,30 @@ struct Workspace {
 std::mutex g_mu;
 std::map<std::pair<int, void*>, Workspace> g_ws;
 
+// mha_fwd_noalloc's workspace: a file-scope device array (one copy per GPU,
+// held until the process ends).  Host code never uses its name as an
+// address: each device's copy is located once with hipGetSymbolAddress, on
+// that device's first call, and that pointer is what the kernels get.
+constexpr size_t kNoAllocBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kNoAllocBytes];
+constexpr int kMaxDevices = 64;
+char* g_noalloc_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (dev is the current device).
+hipError_t noalloc_workspace(int dev, char** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_noalloc_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_noalloc_ptr[dev];
+  return hipSuccess;
+}
+
 constexpr size_t kStateBytes = (sizeof(mha::SchedState) + 255) / 256 * 256;
 static_assert(alignof(mha::SchedState) <= 256, "workspace base is 256-byte aligned");
 
@@ -193,7 +217,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
              int32_t num_kv_heads, int32_t head_dim_nope, int32_t head_dim_rope, int32_t v_dim,
              const void* q_rope, const void* k_rope, int32_t causal, float softmax_scale,
              int32_t dtype, const float* q_scale, const float* k_scale, int32_t total_tokens,
-             int32_t num_splits, float* o_part, float* lse_part, void* stream) {
+             int32_t num_splits, float* o_part, float* lse_part, void* stream,
+             bool noalloc = false) {
   int rc = check_scalars(batch, max_seqlen, num_heads, num_kv_heads);
   if (rc) return rc;
   if (head_dim_nope < 1 || head_dim_rope < 0 || v_dim < 1)
@@ -239,7 +264,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   // tokens; the merge stops at the real total, cu_seqlens[batch])
   // (also under mha_fwd_splitkv with num_splits = 1, which is mha_fwd exactly;
   // its partial buffers are not used then)
-  const bool auto_split = num_splits == 1 && var->launch_split != nullptr;
+  // (not under mha_fwd_noalloc, whose workspace holds no partials)
+  const bool auto_split = num_splits == 1 && var->launch_split != nullptr && !noalloc;
   size_t part_bytes = 0;
   if (auto_split) {
     const int sp = auto_splits(batch, max_seqlen, num_heads, causal, v_dim, var->block_m,
@@ -260,8 +286,17 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   const float sigma =
       softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)(head_dim_nope + head_dim_rope));
   char* ws = nullptr;
-  e = get_workspace(dev, s, plan.bytes + part_bytes, &ws);
-  if (e != hipSuccess) return fail_hip(e, "workspace allocation");
+  if (noalloc) {
+    if (plan.bytes > kNoAllocBytes)
+      return fail(MHA_ERR_INVALID_ARG,
+                  "mha_fwd_noalloc: the work table needs " + std::to_string(plan.bytes) +
+                      " bytes; its fixed workspace holds " + std::to_string(kNoAllocBytes));
+    e = noalloc_workspace(dev, &ws);
+    if (e != hipSuccess) return fail_hip(e, "mha_fwd_noalloc: workspace lookup");
+  } else {
+    e = get_workspace(dev, s, plan.bytes + part_bytes, &ws);
+    if (e != hipSuccess) return fail_hip(e, "workspace allocation");
+  }
   if (split_here) {
     o_part = reinterpret_cast<float*>(ws + plan.bytes);
     lse_part = reinterpret_cast<float*>(
@@ -270,12 +305,12 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   }
   auto* st = reinterpret_cast<mha::SchedState*>(ws);
   auto* table = reinterpret_cast<mha::i32x4*>(ws + kStateBytes);
-  auto* scratch = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
+  auto* gwork = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
 
   const int chunk = mha::prepass_chunk(causal, num_heads / num_kv_heads);
   e = mha::launch_prepass(cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads, causal,
                           var->block_m, var->block_n, num_splits, plan.capacity, chunk, table, st,
-                          scratch, s);
+                          gwork, s);
   if (e != hipSuccess) return fail_hip(e, "scheduler prepass launch");
 
   mha::AttnParams p;
@@ -338,6 +373,18 @@ int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   return fwd_impl(q, k, v, o, lse, cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads,
                   head_dim_nope, head_dim_rope, v_dim, q_rope, k_rope, causal, softmax_scale,
                   dtype, q_scale, k_scale, 0, 1, nullptr, nullptr, stream);
+}
+
+int mha_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim_nope,
+                    int32_t head_dim_rope, int32_t v_dim, const void* q_rope, const void* k_rope,
+                    int32_t causal, float softmax_scale, int32_t dtype, const float* q_scale,
+                    const float* k_scale, void* stream) {
+  g_err.clear();
+  return fwd_impl(q, k, v, o, lse, cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads,
+                  head_dim_nope, head_dim_rope, v_dim, q_rope, k_rope, causal, softmax_scale,
+                  dtype, q_scale, k_scale, 0, 1, nullptr, nullptr, stream, true);
 }
 
 int mha_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -445,10 +492,10 @@ int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen
   if (e != hipSuccess) return fail_hip(e, "workspace allocation");
   auto* st = reinterpret_cast<mha::SchedState*>(ws);
   auto* table = reinterpret_cast<mha::i32x4*>(ws + kStateBytes);
-  auto* scratch = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
+  auto* gwork = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
   const int chunk = mha::prepass_chunk(causal, num_heads / num_kv_heads);
   e = mha::launch_prepass(cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads, causal, block_m,
-                          block_n, 1, plan.capacity, chunk, table, st, scratch, s);
+                          block_n, 1, plan.capacity, chunk, table, st, gwork, s);
   if (e != hipSuccess) return fail_hip(e, "scheduler prepass launch");
   if (grid == 0) grid = cu_count(dev) * 2;
   const int tiles = (int)(((long long)max_seqlen + block_m - 1) / block_m);

@@ -145,6 +145,53 @@ def mha_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
     return o, lse_t
 
 
+def mha_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *,
+                    out: torch.Tensor, lse: torch.Tensor, cu_seqlens: torch.Tensor,
+                    max_seqlen: int, causal: bool = False,
+                    q_rope: Optional[torch.Tensor] = None,
+                    k_rope: Optional[torch.Tensor] = None,
+                    q_scale: Optional[torch.Tensor] = None,
+                    k_scale: Optional[torch.Tensor] = None,
+                    softmax_scale: Optional[float] = None,
+                    fp8_fast_accum: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mha_fwd_noalloc of the C ABI: mha_fwd on the library's fixed workspace,
+    allocating nothing on the device (packed [T, H, D] inputs only; out [T,
+    Hq, Dv] and lse [Hq, T] must be given).  Returns (out, lse)."""
+    if fp8_fast_accum and q.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise ValueError("fp8_fast_accum applies to fp8 inputs only")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [T, H, D]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    code = nat.MHA_DTYPE_FP8_E4M3_FASTACC if fp8_fast_accum else _dtype_code(q)
+    T, Hq, Dn = q.shape
+    Hkv, Dv = k.shape[1], v.shape[2]
+    Dr = 0 if q_rope is None else q_rope.shape[2]
+    vdt = torch.float32 if code == nat.MHA_DTYPE_F32 else torch.bfloat16
+    B = cu_seqlens.numel() - 1
+    _need(q, "q", dev)
+    _need(k, "k", dev, q.dtype, (T, Hkv, Dn))
+    _need(v, "v", dev, vdt, (T, Hkv, Dv))
+    _need(q_rope, "q_rope", dev, vdt, (T, Hq, Dr) if Dr else None)
+    _need(k_rope, "k_rope", dev, vdt, (T, Hkv, Dr) if Dr else None)
+    _need(q_scale, "q_scale", dev, torch.float32, (T, Hq) if q_scale is not None else None)
+    _need(k_scale, "k_scale", dev, torch.float32, (T, Hkv) if k_scale is not None else None)
+    _need(cu_seqlens, "cu_seqlens", dev, torch.int32, (B + 1,))
+    _need(out, "out", dev, vdt, (T, Hq, Dv))
+    _need(lse, "lse", dev, torch.float32, (Hq, T))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    scale_arg = float(softmax_scale) if softmax_scale is not None else 0.0
+    with torch.cuda.device(dev):
+        st = nat.load().mha_fwd_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), int(B),
+            int(max_seqlen), int(Hq), int(Hkv), int(Dn), int(Dr), int(Dv), _ptr(q_rope),
+            _ptr(k_rope), int(bool(causal)), scale_arg, code, _ptr(q_scale), _ptr(k_scale),
+            stream)
+    nat.check(st)
+    return out, lse
+
+
 def mha_fwd_supported(dtype_code: int, head_dim_nope: int, head_dim_rope: int, v_dim: int) -> bool:
     return bool(nat.load().mha_fwd_supported(dtype_code, head_dim_nope, head_dim_rope, v_dim))
 

@@ -147,6 +147,36 @@ int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
             int32_t causal, float softmax_scale, int32_t dtype,
             const float* q_scale, const float* k_scale, void* stream);
 
+/*
+ * mha_fwd_noalloc -- mha_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, results and errors as mha_fwd, except:
+ *
+ *   - the scheduler workspace is a fixed 16 MiB device array inside the
+ *     library (one copy per GPU, held until the process ends), so no call
+ *     allocates or frees device memory; a call whose work table would not
+ *     fit (16 bytes per work item -- num_heads * batch * ceil(max_seqlen /
+ *     block_m), block_m 256 for bf16 / fp8 and 64 for float32 -- plus 4 bytes
+ *     per (sequence, KV head) and 2.3 KB) returns MHA_ERR_INVALID_ARG with a
+ *     message giving both sizes, before any launch;
+ *   - it never splits keys by itself (mha_fwd's own splits keep float32
+ *     partials in its allocated workspace); with one split its output is
+ *     mha_fwd's bit for bit;
+ *   - the first call on a device looks the array up for that device
+ *     (hipGetSymbolAddress; no allocation);
+ *   - every call on one GPU shares that GPU's array: calls that overlap on
+ *     one GPU (two streams, or two host threads) race and must be ordered by
+ *     the caller.  Each call's scheduler prepass rewrites all of the state it
+ *     reads, so calls in sequence need no clearing.
+ */
+int mha_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
+                    int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim_nope, int32_t head_dim_rope, int32_t v_dim,
+                    const void* q_rope, const void* k_rope,
+                    int32_t causal, float softmax_scale, int32_t dtype,
+                    const float* q_scale, const float* k_scale, void* stream);
+
 /* Message for the calling thread's last nonzero status ("" if none).  The
  * string is owned by the library and valid until the thread's next call. */
 const char* mha_fwd_last_error(void);
