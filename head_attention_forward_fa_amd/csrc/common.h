@@ -142,7 +142,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // the same path; only lane 0 touches the counters).  Queue choice is
 // XCD-aware: workgroup i is dispatched to XCD i % 8, so it drains queue
 // i % 8 first (whose items share K/V and therefore that XCD's L2), then the
-// others.  Two ways to drive it:
+// others that still have work.  Two ways to drive it:
 //   take()              the entry of the index reserved before, and a
 //                       reservation of the next one (one item ahead);
 //   reserve(), resolve() the reservation and the entry read as two steps,
@@ -152,8 +152,8 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 //                       queue order) while neither memory round trip sits
 //                       between two items.
 struct Fetcher {
-  int queue, tried, cnt, base;  // wave-uniform
-  int pend;                     // lane 0: the reserved index (in flight until resolved)
+  int queue, cnt, base;  // wave-uniform
+  int pend;              // lane 0: the reserved index (in flight until resolved)
 
   __device__ __forceinline__ void open_queue(const SchedState* st) {
     cnt = __builtin_amdgcn_readfirstlane(st->q[queue].count);
@@ -165,18 +165,40 @@ struct Fetcher {
   }
   __device__ __forceinline__ void init(SchedState* st) {
     queue = blockIdx.x % kNumXcd;
-    tried = 0;
     open_queue(st);
     reserve(st);
   }
-  // Entry of the reserved index, moving on to the next queue (and reserving
-  // there) while this one is exhausted; L = -1 when every queue is.
+  // The first queue after the current one (in queue order, wrapping round
+  // to the current one last) whose counter has not reached its count, or -1
+  // when every queue is drained.  All queues are read at once (lane i reads
+  // queue + 1 + i), with loads that go past the compute unit's cache to the
+  // L2 where the atomic adds happen, so a drained workgroup finds the work
+  // left, or that there is none, in one round trip instead of visiting the
+  // queues one by one.
+  __device__ __forceinline__ int next_open_queue(SchedState* st) {
+    const int lane = __lane_id();
+    bool open = false;
+    if (lane < kNumXcd) {
+      const int qq = (queue + 1 + lane) % kNumXcd;
+      const int c = __hip_atomic_load(&st->q[qq].counter, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      open = c < st->q[qq].count;
+    }
+    const uint64_t b = __builtin_amdgcn_ballot_w64(open);
+    if (b == 0) return -1;
+    return (queue + 1 + (int)__builtin_ctzll(b)) % kNumXcd;
+  }
+  // Entry of the reserved index; while the queue is exhausted, moves to the
+  // next queue that has work left (and reserves there); L = -1 when every
+  // queue is drained.  A reservation that loses the race for a queue's last
+  // items only moves that counter past its count, so the scan ends.
   __device__ __forceinline__ i32x4 resolve(SchedState* st, const i32x4* table) {
     for (;;) {
       const int idx = __builtin_amdgcn_readfirstlane(pend);
       if (idx < cnt) return table[base + idx];
-      if (++tried >= kNumXcd) return i32x4{0, -1, 0, 0};
-      queue = (queue + 1) % kNumXcd;
+      const int nq = next_open_queue(st);
+      if (nq < 0) return i32x4{0, -1, 0, 0};
+      queue = nq;
       open_queue(st);
       reserve(st);
     }
@@ -191,8 +213,9 @@ struct Fetcher {
         reserve(st);
         return e;
       }
-      if (++tried >= kNumXcd) return i32x4{0, -1, 0, 0};
-      queue = (queue + 1) % kNumXcd;
+      const int nq = next_open_queue(st);
+      if (nq < 0) return i32x4{0, -1, 0, 0};
+      queue = nq;
       open_queue(st);
       reserve(st);
     }
