@@ -60,42 +60,50 @@ METRIC = "attention fwd TFLOP/s (4·B·H·Sq·Sk·D, causal halved) and % of MFM
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 
 
-KERNEL = "attn_fwd_mfma_kernel"
+KERNEL = "attn_fwd_mfma_kernel"      # bf16 and fp8 Q/K
+KERNEL_F32 = "attn_fwd_f32_kernel"   # float32
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 COPY_PROBE_MIB = 1024
 
 
-# the sources that decide what the attention kernel and its scheduler do on
+# the sources that decide what each attention kernel and its scheduler do on
 # the device (kernels.h holds the queue chunk rule; the other entry points of
 # the library do not matter)
-KERNEL_SOURCES = ("attn_bf16.hip", "attn_fp8.hip", "attn_mfma.h", "common.h", "kernels.h",
-                  "sched.hip")
+KERNEL_SOURCES = {
+    KERNEL: ("attn_bf16.hip", "attn_fp8.hip", "attn_mfma.h", "common.h", "kernels.h",
+             "sched.hip"),
+    KERNEL_F32: ("attn_f32.hip", "common.h", "kernels.h", "sched.hip"),
+}
 
 
-def kernel_sources_sha256() -> str:
-    """Hash of the attention kernel's sources: a traffic figure is valid for
+def kernel_of(dtype: str) -> str:
+    return KERNEL_F32 if dtype == "f32" else KERNEL
+
+
+def kernel_sources_sha256(kernel: str = KERNEL) -> str:
+    """Hash of an attention kernel's sources: a traffic figure is valid for
     these only."""
     h = hashlib.sha256()
     src = os.path.join(ROOT, "head_attention_forward_fa_amd", "csrc")
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         h.update(f.encode())
         with open(os.path.join(src, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def profile_path(workload: str) -> str:
-    return os.path.join(PROFILE_DIR, f"{KERNEL}_{workload}.md")
+def profile_path(workload: str, kernel: str = KERNEL) -> str:
+    return os.path.join(PROFILE_DIR, f"{kernel}_{workload}.md")
 
 
-def traffic_from_profile(workload: str):
+def traffic_from_profile(workload: str, kernel: str = KERNEL):
     """HBM bytes per launch recorded for the current sources, else None."""
-    path = profile_path(workload)
+    path = profile_path(workload, kernel)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"sources_sha256=(\w+)\s+hbm_bytes_per_launch=([0-9.e+]+)", text)
-    if not m or m.group(1) != kernel_sources_sha256():
+    if not m or m.group(1) != kernel_sources_sha256(kernel):
         return None
     return float(m.group(2))
 
@@ -142,6 +150,16 @@ def peak_for(inp, fast_accum: bool = False) -> float:
     return PEAK_TFLOPS[inp.dtype]
 
 
+def cpu_model() -> str:
+    """The host CPU's model name and logical CPU count (Linux)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            names = [ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")]
+    except OSError:
+        names = []
+    return f"{names[0] if names else 'unknown'} ({len(names) or os.cpu_count()} logical CPUs)"
+
+
 def cpu_baseline(inp, budget_s: float = 10.0):
     """Time the oracle (as it is) on whole (sequence, head) pairs."""
     import oracle
@@ -182,12 +200,16 @@ def cpu_baseline(inp, budget_s: float = 10.0):
                 break
         if t_used >= budget_s:
             break
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                   if p.get("user_api") == "blas"] or [1])
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    vendor = ", ".join(sorted({f"{p.get('internal_api', '?')} {p.get('version', '')}".strip()
+                               for p in blas})) or "none found"
     return {
         "value": flops / t_used / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "cpu_model": cpu_model(),
+        "blas": vendor,
         "kind": "oracle",
         "sample": (f"{pairs} whole (sequence, head) pairs of {inp.name} "
                    f"({pairs}/{inp.batch * inp.num_heads} of the workload), float64 numpy, "
@@ -217,6 +239,7 @@ def _pmc_per_dispatch(d: str, kernel_substr: str):
 def summarize_profile(prof: str, workload: str) -> str:
     """profiles/<kernel>_<workload>.md from the rocprofv3 runs under prof."""
     inp = mi.workload(workload)
+    KERNEL = kernel_of(inp.dtype)  # noqa: N806 (the profiled kernel)
     stats = _csv_rows(os.path.join(prof, "trace"), "kernel_stats.csv")
     krow = next(r for r in stats if KERNEL in r["Name"])
     prow = [r for r in stats if "sched_prepass" in r["Name"]]
@@ -303,11 +326,12 @@ def summarize_profile(prof: str, workload: str) -> str:
         f"{f_write:.4f} written = {hbm / 1e6:.1f} MB per launch; algorithmic bytes "
         f"{algo / 1e6:.1f} MB (ratio {hbm / algo:.3f}); {hbm / (avg_ns * 1e-9) / 1e9:.0f} GB/s.",
         "",
-        f"traffic: sources_sha256={kernel_sources_sha256()} hbm_bytes_per_launch={hbm:.6e}",
+        f"traffic: sources_sha256={kernel_sources_sha256(KERNEL)} "
+        f"hbm_bytes_per_launch={hbm:.6e}",
         "",
     ]
     os.makedirs(PROFILE_DIR, exist_ok=True)
-    out = profile_path(workload)
+    out = profile_path(workload, KERNEL)
     with open(out, "w") as fh:
         fh.write("\n".join(lines))
     return out
@@ -520,7 +544,7 @@ def main(argv=None):
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (kmean * 1e-3) / 1e12
     peak = peak_for(inp, fast)
-    traffic = traffic_from_profile(inp.name + ("_fastacc" if fast else ""))
+    traffic = traffic_from_profile(inp.name + ("_fastacc" if fast else ""), kernel_of(inp.dtype))
     print(f"[bench] {ms_per_step * 1e3:.1f} us/step, attention kernel mean {kmean * 1e3:.1f} us "
           f"(min {min(kernel_ms) * 1e3:.1f}), {value:.1f} TFLOP/s, {100 * achieved / peak:.1f}% "
           f"of {peak:.0f}", file=sys.stderr, flush=True)

@@ -477,7 +477,7 @@ int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen
   else if (block_m == mha::kBlockM_F32)
     block_n = mha::kBlockN_F32;
   else
-    return fail(MHA_ERR_INVALID_ARG, "block_m must be 64 or 256");
+    return fail(MHA_ERR_INVALID_ARG, "block_m must be 32 or 256");
   if (grid < 0) return fail(MHA_ERR_INVALID_ARG, "grid must be >= 0");
   if (max_seqlen == 0) return MHA_OK;
   Plan plan;

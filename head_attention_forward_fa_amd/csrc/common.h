@@ -142,15 +142,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // the same path; only lane 0 touches the counters).  Queue choice is
 // XCD-aware: workgroup i is dispatched to XCD i % 8, so it drains queue
 // i % 8 first (whose items share K/V and therefore that XCD's L2), then the
-// others that still have work.  Two ways to drive it:
-//   take()              the entry of the index reserved before, and a
-//                       reservation of the next one (one item ahead);
-//   reserve(), resolve() the reservation and the entry read as two steps,
-//                       which a kernel places near the end of its current
-//                       item, so that the next item is chosen late (the
-//                       queue then deals like a list scheduler over the
-//                       queue order) while neither memory round trip sits
-//                       between two items.
+// others that still have work.  It is driven in two steps, reserve() (an
+// atomic add whose result is not waited for) and resolve() (the entry of
+// the reserved index), which a kernel places apart inside its current item
+// so that neither memory round trip sits between two items: the bf16 / fp8
+// kernel near the item's end (the next item is then chosen late, and the
+// queue deals like a list scheduler over the queue order), the float32
+// kernel at the item's start and after its key blocks.
 struct Fetcher {
   int queue, cnt, base;  // wave-uniform
   int pend;              // lane 0: the reserved index (in flight until resolved)
@@ -196,23 +194,6 @@ struct Fetcher {
     for (;;) {
       const int idx = __builtin_amdgcn_readfirstlane(pend);
       if (idx < cnt) return table[base + idx];
-      const int nq = next_open_queue(st);
-      if (nq < 0) return i32x4{0, -1, 0, 0};
-      queue = nq;
-      open_queue(st);
-      reserve(st);
-    }
-  }
-  // resolve(), plus a reservation of the next index once an entry is found
-  // (issued without waiting for the entry's table read)
-  __device__ __forceinline__ i32x4 take(SchedState* st, const i32x4* table) {
-    for (;;) {
-      const int idx = __builtin_amdgcn_readfirstlane(pend);
-      if (idx < cnt) {
-        const i32x4 e = table[base + idx];
-        reserve(st);
-        return e;
-      }
       const int nq = next_open_queue(st);
       if (nq < 0) return i32x4{0, -1, 0, 0};
       queue = nq;

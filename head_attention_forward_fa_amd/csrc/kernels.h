@@ -12,7 +12,7 @@ namespace mha {
 // Query-tile heights of the two kernel families (rows of Q per work item).
 constexpr int kBlockM_Mfma = 256;
 constexpr int kBlockN_Mfma = 64;
-constexpr int kBlockM_F32 = 64;
+constexpr int kBlockM_F32 = 32;
 constexpr int kBlockN_F32 = 32;
 
 // chunk: groups per chunk of a queue (>= 1), see prepass_chunk.
@@ -37,8 +37,8 @@ inline int prepass_chunk(int causal, int group) {
   return causal ? (group >= 8 ? 1 : 8 / group) : 1;
 }
 
-// protocol: 0 take(), 1 reserve() / resolve() placed as the attention kernel
-// places them (see sched_visit_kernel)
+// protocol: 0 reserve() / resolve() placed as the float32 kernel places
+// them, 1 as the bf16 / fp8 kernel does (see sched_visit_kernel)
 hipError_t launch_sched_visit(int batch, int num_heads, int tiles, int protocol,
                               const i32x4* table, SchedState* st, int* visits, int grid,
                               hipStream_t stream);

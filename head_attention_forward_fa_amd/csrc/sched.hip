@@ -318,8 +318,9 @@ __global__ __launch_bounds__(kPrepassThreads) void sched_prepass_kernel(
   }
 }
 
-// protocol 0: take() (the next item reserved when the current one starts);
-// protocol 1: reserve() and resolve() as two steps at the places the
+// protocol 0: the next item reserved when the current one starts and its
+// entry read after a workgroup barrier (the float32 kernel's placement);
+// protocol 1: reserve() and resolve() at the places the matrix-core
 // attention kernel uses them: an item of nb key blocks (here nb = qt % 5, so
 // that items with no blocks occur too) reserves at block max(0, nb - 3) and
 // reads the entry at block max(0, nb - 1), with a workgroup barrier per block;
@@ -334,7 +335,7 @@ __global__ __launch_bounds__(256) void sched_visit_kernel(int batch, int num_hea
   const bool w0 = threadIdx.x < kWave;
   if (w0) {
     fetch.init(st);
-    const i32x4 e0 = protocol ? fetch.resolve(st, table) : fetch.take(st, table);
+    const i32x4 e0 = fetch.resolve(st, table);
     if (threadIdx.x == 0) s_item[0] = e0;
   }
   for (int it = 0;; ++it) {
@@ -344,7 +345,9 @@ __global__ __launch_bounds__(256) void sched_visit_kernel(int batch, int num_hea
     const WorkItem w = decode_item(e);
     i32x4 nxt = {0, -1, 0, 0};
     if (protocol == 0) {
-      if (w0) nxt = fetch.take(st, table);
+      if (w0) fetch.reserve(st);
+      __syncthreads();
+      if (w0) nxt = fetch.resolve(st, table);
     } else {
       const int nb = w.qt % 5;
       const int j_res = max(0, nb - 3), j_get = max(0, nb - 1);

@@ -211,8 +211,9 @@ def mha_sched_visit(cu_seqlens: torch.Tensor, max_seqlen: int, num_heads: int,
                     num_kv_heads: int, causal: bool, block_m: int = 256,
                     grid: int = 0, protocol: int = 1) -> torch.Tensor:
     """Runs the scheduler alone; returns visit counts [Hq, B, tiles] (int32).
-    protocol 0: next item fetched when an item starts; 1: reserved and read
-    near the end of an item, as the matrix-core kernel does."""
+    protocol 0: next item reserved when an item starts and read after the
+    item's work, as the float32 kernel does; 1: reserved and read near the end
+    of an item, as the matrix-core kernel does."""
     B = cu_seqlens.numel() - 1
     tiles = (max_seqlen + block_m - 1) // block_m
     visits = torch.zeros((num_heads, B, max(tiles, 1)), dtype=torch.int32,

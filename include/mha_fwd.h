@@ -84,7 +84,7 @@ typedef enum {
  *               (that would need a device sync).
  *   batch       number of sequences, >= 1
  *   max_seqlen  >= every sequence length; sizes the work table (num_heads *
- *               batch * ceil(max_seqlen / block_m) entries, block_m = 64
+ *               batch * ceil(max_seqlen / block_m) entries, block_m = 32
  *               for float32 and 256 for bf16 / fp8).  0 means every
  *               sequence is empty: the scalar arguments are still checked,
  *               but nothing is read, written or launched and the tensor
@@ -156,7 +156,7 @@ int mha_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *     library (one copy per GPU, held until the process ends), so no call
  *     allocates or frees device memory; a call whose work table would not
  *     fit (16 bytes per work item -- num_heads * batch * ceil(max_seqlen /
- *     block_m), block_m 256 for bf16 / fp8 and 64 for float32 -- plus 4 bytes
+ *     block_m), block_m 256 for bf16 / fp8 and 32 for float32 -- plus 4 bytes
  *     per (sequence, KV head) and 2.3 KB) returns MHA_ERR_INVALID_ARG with a
  *     message giving both sizes, before any launch;
  *   - it never splits keys by itself (mha_fwd's own splits keep float32
@@ -220,12 +220,13 @@ int mha_fwd_set_kernel_events(void* start_event, void* stop_event);
  * this block_m) that only fetch work items and add 1 to
  * visits[h * (batch * tiles) + b * tiles + qtile], tiles =
  * ceil(max_seqlen / block_m).  visits is a caller-owned device int32 array of
- * num_heads * batch * tiles entries, zeroed by the caller.  block_m is 64 or
- * 256 (the float32 and MFMA kernels' query tiles).  protocol 0 fetches the
- * next item when the current one starts (as the float32 kernel does);
- * protocol 1 reserves it and reads its entry as two separate steps near the
- * end of the current item, with workgroup barriers in between (as the
- * matrix-core kernel does; items with no key blocks included).  Every
+ * num_heads * batch * tiles entries, zeroed by the caller.  block_m is 32 or
+ * 256 (the float32 and bf16 / fp8 kernels' query tiles).  protocol 0
+ * reserves the next item when the current one starts and reads its entry
+ * after a workgroup barrier (as the float32 kernel does); protocol 1 reserves
+ * it and reads its entry near the end of the current item, with workgroup
+ * barriers in between (as the bf16 / fp8 kernel does; items with no key
+ * blocks included).  Every
  * existing item must end with exactly one visit.  MHA_ERR_INVALID_ARG for a
  * protocol other than 0 or 1.
  */

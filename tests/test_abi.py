@@ -106,7 +106,7 @@ def test_supported_set():
 
 def test_sched_visit_validation():
     lib = nat.load()
-    for bad_block_m in (32, 128):
+    for bad_block_m in (64, 128):
         assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, bad_block_m, 0, 1, FAKE,
                                    None) == nat.MHA_ERR_INVALID_ARG
     assert lib.mha_sched_visit(FAKE, 1, 16, 4, 2, 1, 256, 0, 1, None, None) == nat.MHA_ERR_INVALID_ARG

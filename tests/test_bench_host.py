@@ -28,3 +28,19 @@ def test_fast_fp8_is_rated_at_the_time_weighted_blend():
         256 / (128 / 5000 + 128 / 2500))
     assert bench.peak_for(_inp("fp8", dr=64), fast_accum=True) == pytest.approx(
         320 / (128 / 5000 + 192 / 2500))
+
+
+def test_profiled_kernel_follows_the_dtype():
+    assert bench.kernel_of("f32") == "attn_fwd_f32_kernel"
+    for dt in ("bf16", "fp8"):
+        assert bench.kernel_of(dt) == "attn_fwd_mfma_kernel"
+    # a profile summary is keyed by kernel and workload, and its source hash
+    # covers that kernel's own sources
+    assert bench.profile_path("w", "attn_fwd_f32_kernel").endswith("attn_fwd_f32_kernel_w.md")
+    assert bench.kernel_sources_sha256("attn_fwd_f32_kernel") != bench.kernel_sources_sha256(
+        "attn_fwd_mfma_kernel")
+
+
+def test_cpu_model_names_the_host():
+    s = bench.cpu_model()
+    assert "logical CPUs" in s and len(s) > 20

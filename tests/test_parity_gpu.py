@@ -40,6 +40,10 @@ SMALL = [
     ("f32", [70], 2, 1, 128, 64, 128, True),
     ("f32", [130, 1], 2, 2, 64, 0, 64, True),
     ("f32", [130, 1], 2, 2, 64, 0, 64, False),
+    ("f32", [300, 1, 0, 129, 64], 8, 2, 64, 0, 64, True),
+    ("f32", [300, 1, 0, 129, 64], 8, 2, 64, 0, 64, False),
+    ("f32", [517, 33], 4, 2, 128, 0, 128, False),
+    ("f32", [260, 31], 2, 2, 128, 64, 128, False),
     # more items than workgroups (about 1 000 against 256): every workgroup
     # runs several items in a row, so whatever an item carries over to the
     # next (its Q fragments, the fp8 q_scale multiplier, the next item's
@@ -47,6 +51,7 @@ SMALL = [
     ("fp8", [300, 257, 40, 512] * 8, 16, 4, 128, 0, 128, True),
     ("bf16", [300, 257, 40, 512] * 8, 16, 4, 128, 0, 128, True),
     ("bf16", [300, 257, 40, 512] * 8, 16, 16, 128, 64, 128, True),
+    ("f32", [300, 257, 40, 512] * 4, 8, 2, 64, 0, 64, True),
 ]
 
 
@@ -199,11 +204,12 @@ def test_overflowing_lengths_are_refused_without_writes():
     assert bool((out == 7.0).all()) and bool((lse == 7.0).all())
 
 
-# protocol 0: the next item fetched when an item starts (the float32 kernel);
+# protocol 0: the next item reserved when an item starts, its entry read after
+# a barrier (the float32 kernel);
 # protocol 1: reserved and read in two steps near the end of an item, items
 # with no key blocks included (the matrix-core kernel)
 @pytest.mark.parametrize("protocol", [0, 1])
-@pytest.mark.parametrize("block_m", [64, 256])
+@pytest.mark.parametrize("block_m", [32, 256])
 @pytest.mark.parametrize("grid", [0, 1, 7, 1000])
 def test_scheduler_visits_every_item_once(block_m, grid, protocol):
     from head_attention_forward_fa_amd import mha_sched_visit
