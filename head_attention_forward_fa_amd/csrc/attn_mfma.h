@@ -99,11 +99,16 @@ struct MfmaCfg {
   static constexpr int BN = kBlockN_Mfma;  // 64 keys per block
   static constexpr int WAVES = BM / 32;    // 8 waves, two per SIMD
   static constexpr int THREADS = WAVES * kWave;
-  // SD: exact fp8 without a rope part decodes each K block once, for the
-  // whole workgroup: the fp8 rows land in a staging ring and are written
-  // back as bfloat16 rows into the K ring, which the products then read as
-  // in the bf16 kernel
-  static constexpr bool SD = FP8 && !F8MMA && DR == 0;
+  // SD: exact fp8 decodes each K block once, for the whole workgroup: the
+  // fp8 nope rows land in a staging ring and are written back as bfloat16
+  // rows into the K ring, which the products then read as in the bf16
+  // kernel.  With a rope part (SDR) the K block is staged by depth: the
+  // nope depth through the staging ring and the decode, the bfloat16 rope
+  // depth straight into its K slot one block later (the depth-staged K of
+  // the pages' TMAProducerPipeline, K staged in num_qk_stages chunks), so
+  // that the decoded ring fits in 160 KiB (see NSS, JUNK).
+  static constexpr bool SD = FP8 && !F8MMA;
+  static constexpr bool SDR = SD && DR > 0;
   static constexpr int EB = FP8 ? 1 : 2;   // bytes per Q/K nope element
   static constexpr int K_HB = DN * EB;     // bytes per K nope row in HBM
   static constexpr int K_RB = SD ? DN * 2 : K_HB;  // bytes per K nope row in a K slot
@@ -120,19 +125,31 @@ struct MfmaCfg {
   static constexpr int KS_OFF = R_OFF + BN * R_RP;     // inside a K slot
   static constexpr int KSLOT = (KS_OFF + (FP8 ? 256 : 0) + 255) / 256 * 256;
   static constexpr int VSLOT = BN * V_RB;
-  // SD staging slot: fp8 rows (unpadded), k_scale
-  static constexpr int NSS = SD ? 3 : 0;
+  // SD staging slot: fp8 rows (unpadded), k_scale.  3 slots (staged four
+  // blocks ahead); SDR: 2 (staged three blocks ahead, two slots being what
+  // fits next to the decoded K ring with its rope rows and the V ring)
+  static constexpr int NSS = SD ? (SDR ? 2 : 3) : 0;
   static constexpr int SSLOT = SD ? BN * K_HB + 256 : 0;
   // 4 K slots when they fit next to the V ring, else 3 (the rope layout);
   // SD: 3 (a decoded block is written one block before its first use)
   static constexpr int NKS =
       SD ? 3 : 4 * KSLOT + NVS * BN * V_RB + 1024 + 64 <= 160 * 1024 ? 4 : 3;
-  // blocks between a K block's request and its use (SD: its decode)
-  static constexpr int KLEAD = SD ? 4 : NKS - 1;
+  // blocks between a K block's request and its use (SD: the staged rows'
+  // request and their decode); RLEAD: the same for the rope rows, which
+  // SDR requests into their K slot directly
+  static constexpr int KLEAD = SD ? (SDR ? 3 : 4) : NKS - 1;
+  static constexpr int RLEAD = SDR ? 2 : KLEAD;
+  // batch j's K-side DMA may still be in flight at barrier j (its data is
+  // first used, or decoded, after barrier j + 1)
+  static constexpr bool K_SLACK = KLEAD >= 3 && !SDR;
   static constexpr int S_BASE = NKS * KSLOT;
   static constexpr int V_BASE = S_BASE + NSS * SSLOT;
-  static constexpr int JUNK = V_BASE + NVS * VSLOT;  // 1 KiB sink for padding DMA ops
-  static constexpr int LDS = JUNK + 1024;
+  // 1 KiB sink for DMA ops past a region's end.  SDR has none (160 KiB):
+  // such ops repeat the region's last instruction, the same bytes to the
+  // same place, and the k_scale op of every wave is wave 0's.
+  static constexpr bool NOJUNK = SDR;
+  static constexpr int JUNK = V_BASE + NVS * VSLOT;
+  static constexpr int LDS = JUNK + (NOJUNK ? 0 : 1024);
   static constexpr int OCC = 1;              // one workgroup (8 waves) per CU
   static constexpr int O_ROW = DV * 2 + 16;  // epilogue staging row stride
   static constexpr int QK_STEPS = F8MMA ? DN / 64 : DN / 16;  // nope MFMA k-steps
@@ -145,9 +162,10 @@ struct MfmaCfg {
   // (DW of them, one per SIMD) issue them: wave w takes instructions w,
   // w + DW, ... of each region (the fp8 k_scale: wave 0, one dword per
   // lane).  Each of them issues the same N_OPS instructions per block: the
-  // ones past a region's end, another wave's k_scale and those of a block
-  // that does not exist read nothing (empty buffer range) and land in the
-  // JUNK sink, so one vmcnt(N_OPS) wait fits every wave and every block.
+  // ones past a region's end and another wave's k_scale read nothing and
+  // land in the JUNK sink (NOJUNK: they repeat an existing instruction), and
+  // those of a block that does not exist read nothing (empty buffer range),
+  // so one vmcnt(N_OPS) wait fits every wave and every block.
   static constexpr int DW = WAVES / 2;
   static constexpr int K_INST = SD ? BN * K_HB / 1024 : BN * K_RP / 1024;
   static constexpr int R_INST = BN * R_RP / 1024;
@@ -273,13 +291,24 @@ struct MfmaKernel {
     const int row = q / UPR, chunk = q % UPR;
     return chunk == UPR - 1 ? 0x80000000u : (uint32_t)(row * row_stride + chunk * 16);
   }
+  // SD staging order: 16-byte unit u of a staged block (u = 64 n + i for
+  // lane i of DMA instruction n, and thread u of the decode) holds chunk
+  // sd_chunk(u) of row sd_row(u): each group of 8 units is one chunk of 8
+  // consecutive rows, and units 8 apart take chunks 4 apart.  The decode's
+  // 16-byte writes to the padded K rows (pitch K_HB * 2 + 16) then fall on
+  // distinct banks within every 8 and every 16 lanes, and its reads are
+  // consecutive.
+  static __device__ __forceinline__ int sd_row(int u) { return 8 * (u >> 6) + (u & 7); }
+  static __device__ __forceinline__ int sd_chunk(int u) {
+    const int j = (u >> 3) & 7;
+    return (j >> 1) | ((j & 1) << 2);
+  }
   // Per-lane source offset of DMA instruction n of an unpadded K staging
-  // region (SD): lane i fills 16-byte unit 64n + i, i.e. chunk (64n + i) %
-  // (K_HB/16) of row (64n + i) / (K_HB/16).
+  // region (SD): lane i fills unit 64n + i (see sd_row, sd_chunk).
   static __device__ __forceinline__ uint32_t dma_s_lane_off(int n, int lane, int row_stride) {
-    constexpr int UPR = C::K_HB / 16;
-    const int q = 64 * n + lane;
-    return (uint32_t)((q / UPR) * row_stride + (q % UPR) * 16);
+    static_assert(!C::SD || C::K_HB == 128, "SD staging: 8 chunks of 16 bytes per row");
+    const int u = 64 * n + lane;
+    return (uint32_t)(sd_row(u) * row_stride + sd_chunk(u) * 16);
   }
   // Per-lane source offset of DMA instruction n of an unpadded, swizzled V
   // region: instruction n covers rows RPI*n .. RPI*n+RPI-1; lane i fills
@@ -296,7 +325,9 @@ struct MfmaKernel {
   // This wave's DMA source offsets (fixed for the kernel: they depend on the
   // head stride only).  An instruction index past a region's end gets rows
   // past every block (all lanes out of range, zeros); another wave's k_scale
-  // instruction gets lanes out of range too.
+  // instruction gets lanes out of range too.  NOJUNK: both repeat an
+  // existing instruction instead (the rope region's last one, wave 0's
+  // k_scale).
   struct DmaLanes {
     uint32_t k[C::K_DMA];
     uint32_t r[C::R_DMA > 0 ? C::R_DMA : 1];
@@ -312,13 +343,16 @@ struct MfmaKernel {
                      : dma_k_lane_off<C::K_HB>(wave + C::DW * i, lane, Hkv * C::K_HB);
     if constexpr (C::R_DMA > 0) {
 #pragma unroll
-      for (int i = 0; i < C::R_DMA; ++i)
-        d.r[i] = dma_k_lane_off<C::R_RB>(wave + C::DW * i, lane, Hkv * C::R_RB);
+      for (int i = 0; i < C::R_DMA; ++i) {
+        const int n = wave + C::DW * i;
+        d.r[i] = dma_k_lane_off<C::R_RB>(C::NOJUNK && n >= C::R_INST ? C::R_INST - 1 : n, lane,
+                                         Hkv * C::R_RB);
+      }
     }
 #pragma unroll
     for (int i = 0; i < C::V_DMA; ++i)
       d.v[i] = dma_v_lane_off<C::V_RB>(wave + C::DW * i, lane, Hkv * C::V_RB);
-    d.ks = wave == 0 ? (uint32_t)(lane * Hkv * 4) : 0x80000000u;
+    d.ks = wave == 0 || C::NOJUNK ? (uint32_t)(lane * Hkv * 4) : 0x80000000u;
     return d;
   }
 
@@ -353,65 +387,78 @@ struct MfmaKernel {
     return d;
   }
 
-  // One batch of the DMA pipeline: the K side of block kblk and the V of
-  // block vblk (different blocks).  A block that does not exist gets empty
-  // ranges and still its own slot, which nobody reads while it is written.
+  // One batch of the DMA pipeline: the K side of block kblk (its rope rows:
+  // of block rblk) and the V of block vblk (different blocks).  A block that
+  // does not exist gets empty ranges and still its own slot, which nobody
+  // reads while it is written.
   struct BlockDma {
-    i32x4 k, r, ks, v;       // buffer resources
-    uint32_t kdst, vdst;     // this wave's 1 KiB run in the K / V slot
+    i32x4 k, r, ks, v;         // buffer resources
+    uint32_t kdst, rdst, vdst;  // this wave's 1 KiB run in the K (SD: staging) / rope's K / V slot
   };
   template <int RB>
   static __device__ __forceinline__ i32x4 block_rsrc(const char* base, const DmaSrc& d, int blk,
                                                     uint32_t span) {
     return rsrc_of(base + (size_t)((uint32_t)blk * d.rows_stride) * RB, span * RB);
   }
+  // rows a block spans in [T, Hkv] (0: the block is outside the item's range)
+  template <bool SPLIT>
+  static __device__ __forceinline__ uint32_t block_span(const DmaSrc& d, int blk) {
+    if constexpr (SPLIT)
+      return blk >= d.jlo && blk < d.jhi ? (blk < d.nblocks - 1 ? d.span_full : d.span_last) : 0u;
+    else  // the range is [0, nblocks)
+      return blk >= 0 && blk < d.nblocks ? (blk < d.nblocks - 1 ? d.span_full : d.span_last) : 0u;
+  }
   template <bool SPLIT>
   static __device__ __forceinline__ BlockDma block_dma(const DmaSrc& d, uint32_t sbase, int wave,
-                                                      int kblk, int vblk) {
-    uint32_t kspan, vspan;
-    if constexpr (SPLIT) {
-      kspan = kblk >= d.jlo && kblk < d.jhi ? (kblk < d.nblocks - 1 ? d.span_full : d.span_last)
-                                            : 0u;
-      vspan = vblk >= d.jlo && vblk < d.jhi ? (vblk < d.nblocks - 1 ? d.span_full : d.span_last)
-                                            : 0u;
-    } else {  // the range is [0, nblocks); K blocks are never negative
-      kspan = kblk < d.nblocks - 1 ? d.span_full : (kblk == d.nblocks - 1 ? d.span_last : 0u);
-      vspan = vblk >= 0 && vblk < d.nblocks ? (vblk < d.nblocks - 1 ? d.span_full : d.span_last)
-                                            : 0u;
-    }
+                                                      int kblk, int rblk, int vblk) {
+    const uint32_t kspan = block_span<SPLIT>(d, kblk), vspan = block_span<SPLIT>(d, vblk);
     const int kb = kspan ? kblk : 0, vb = vspan ? vblk : 0;  // keep addresses in range
     BlockDma b;
     b.k = block_rsrc<C::K_HB>(d.k, d, kb, kspan);
-    if constexpr (C::DR > 0) b.r = block_rsrc<C::R_RB>(d.r, d, kb, kspan);
+    if constexpr (C::DR > 0) {
+      const uint32_t rspan = C::SDR ? block_span<SPLIT>(d, rblk) : kspan;
+      b.r = block_rsrc<C::R_RB>(d.r, d, rspan ? rblk : 0, rspan);
+    }
     if constexpr (C::FP8) b.ks = block_rsrc<4>(d.ks, d, kb, kspan);
     b.v = block_rsrc<C::V_RB>(d.v, d, vb, vspan);
     b.kdst = (C::SD ? sbase + C::S_BASE + (uint32_t)(kblk % C::NSS) * C::SSLOT
                     : sbase + (uint32_t)(kblk % C::NKS) * C::KSLOT) +
              1024u * (uint32_t)wave;
+    // (rblk >= -KLEAD: the first batches of an item name blocks before it)
+    b.rdst = sbase + (uint32_t)((rblk + 4 * C::NKS) % C::NKS) * C::KSLOT + 1024u * (uint32_t)wave;
     b.vdst = sbase + C::V_BASE + (uint32_t)(vblk & (C::NVS - 1)) * C::VSLOT +
              1024u * (uint32_t)wave;
     return b;
   }
   // DMA op OP of this wave (K nope, K rope, fp8 k_scale, V, in that order).
   // An instruction index past its region's end (for this wave) and another
-  // wave's k_scale instruction write their zeros into the JUNK sink.
+  // wave's k_scale instruction write their zeros into the JUNK sink
+  // (NOJUNK: they repeat the region's last instruction and wave 0's k_scale
+  // instruction, identical bytes to the same place).
   template <int OP>
   static __device__ __forceinline__ void dma_op(const BlockDma& b, const DmaLanes& d,
                                                 uint32_t junk, int wave) {
     if constexpr (OP < C::K_DMA) {
       constexpr uint32_t OFF = C::K_OFF + 1024u * C::DW * OP;
       uint32_t m0 = b.kdst + OFF;
-      if constexpr ((OP + 1) * C::DW > C::K_INST) m0 = wave + C::DW * OP < C::K_INST ? m0 : junk;
+      if constexpr ((OP + 1) * C::DW > C::K_INST) {
+        static_assert(!C::NOJUNK, "K regions of whole instructions per wave");
+        m0 = wave + C::DW * OP < C::K_INST ? m0 : junk;
+      }
       dma16(b.k, m0, d.k[OP]);
     } else if constexpr (OP < C::K_DMA + C::R_DMA) {
       constexpr int I = OP - C::K_DMA;
       constexpr uint32_t OFF = C::R_OFF + 1024u * C::DW * I;
-      uint32_t m0 = b.kdst + OFF;
-      if constexpr ((I + 1) * C::DW > C::R_INST) m0 = wave + C::DW * I < C::R_INST ? m0 : junk;
+      uint32_t m0 = b.rdst + OFF;
+      if constexpr ((I + 1) * C::DW > C::R_INST) {
+        const uint32_t last = b.rdst - 1024u * (uint32_t)wave + C::R_OFF + 1024u * (C::R_INST - 1);
+        m0 = wave + C::DW * I < C::R_INST ? m0 : (C::NOJUNK ? last : junk);
+      }
       dma16(b.r, m0, d.r[I]);
     } else if constexpr (OP < C::K_DMA + C::R_DMA + C::KS_DMA) {
       // wave 0's run starts at its slot's k_scale area
-      dma4(b.ks, wave == 0 ? b.kdst + (C::SD ? C::BN * C::K_HB : C::KS_OFF) : junk, d.ks);
+      const uint32_t ks0 = b.kdst - 1024u * (uint32_t)wave + (C::SD ? C::BN * C::K_HB : C::KS_OFF);
+      dma4(b.ks, wave == 0 || C::NOJUNK ? ks0 : junk, d.ks);
     } else {
       constexpr int I = OP - C::K_DMA - C::R_DMA - C::KS_DMA;
       dma16(b.v, b.vdst + 1024u * C::DW * I, d.v[I]);
@@ -529,15 +576,15 @@ struct MfmaKernel {
 
   // SD: the staged fp8 rows of block blk, decoded to bfloat16 into its K
   // slot (rows at pitch K_RP, as the bf16 kernel stores them), and its
-  // k_scale copied there.  One 16-byte chunk (16 codes) per thread.
+  // k_scale copied there.  One 16-byte unit (16 codes) per thread, in the
+  // staging order of sd_row / sd_chunk.
   static __device__ __forceinline__ void decode_block(uint32_t sbase, int blk, int tid) {
     typedef __attribute__((address_space(3))) i32x4 li32x4;
     typedef __attribute__((address_space(3))) bf16x8 lbf16x8;
     const uint32_t src = sbase + C::S_BASE + (uint32_t)(blk % C::NSS) * C::SSLOT;
     const uint32_t dst = sbase + (uint32_t)(blk % C::NKS) * C::KSLOT;
-    constexpr int CPR = C::K_HB / 16;  // staged chunks per row
-    const int row = tid / CPR, ch = tid % CPR;
-    const i32x4 x = *reinterpret_cast<const li32x4*>(lp(src + row * C::K_HB + ch * 16));
+    const int row = sd_row(tid), ch = sd_chunk(tid);
+    const i32x4 x = *reinterpret_cast<const li32x4*>(lp(src + tid * 16));
     lchar* d = const_cast<lchar*>(lp(dst + row * C::K_RP + ch * 32));
     *reinterpret_cast<lbf16x8*>(d) = dec8(i32x2{x[0], x[1]});
     *reinterpret_cast<lbf16x8*>(d + 16) = dec8(i32x2{x[2], x[3]});
@@ -961,20 +1008,29 @@ struct MfmaKernel {
       w.m = -INFINITY;
       w.l = 0.f;
 
-      // The DMA pipeline: batch t is {K_{t+KLEAD}, V_{t+2}}, and block j
-      // issues batch j.  The prologue issues the batches before block 0:
-      // those needed in block 0 are waited for here together with the Q
-      // loads (the compiler's own wait for those could not tell the DMA
-      // apart anyway); with 4 K slots the last one goes out after the first
-      // S.
+      // The DMA pipeline: batch t is {K_{t+KLEAD} (SDR: its rope rows
+      // K_{t+RLEAD}), V_{t+2}}, and block j issues batch j.  The prologue
+      // issues the batches before block 0: those needed in block 0 are
+      // waited for here together with the Q loads (the compiler's own wait
+      // for those could not tell the DMA apart anyway); with 4 K slots the
+      // last one goes out after the first S.  SDR: the staged rows of block
+      // jlo + 2 go to the staging slot of block jlo, so they are requested
+      // after that block's decode, and waited for before block jlo.
       const int grp = wave >> 2;  // group 0 issues the DMA
       const DmaSrc dsrc = dma_src(p, s0, L, g, nblocks, jlo, jhi);
       auto blk = [&](int t) {
-        return block_dma<SPLIT>(dsrc, sbase, wave, t + C::KLEAD, t + 2);
+        return block_dma<SPLIT>(dsrc, sbase, wave, t + C::KLEAD, t + C::RLEAD, t + 2);
       };
-      if (grp == 0)
+      constexpr int OP_R = C::K_DMA, OP_KS = OP_R + C::R_DMA, OP_V = OP_KS + C::KS_DMA;
+      if (grp == 0) {
         for (int t = jlo - C::KLEAD; t < jlo + (C::KLEAD >= 3 ? -1 : 0); ++t)
           dma_ops<0, C::N_OPS>(blk(t), dl, junk, wave);
+        if constexpr (C::SDR) {
+          const BlockDma b = blk(jlo - 1);
+          dma_ops<OP_R, OP_KS>(b, dl, junk, wave);
+          dma_ops<OP_V, C::N_OPS>(b, dl, junk, wave);
+        }
+      }
       wait_vm<0>();
       __syncthreads();
       if constexpr (C::SD) {
@@ -983,12 +1039,22 @@ struct MfmaKernel {
         decode_block(sbase, jlo + 1, tid);
         __syncthreads();
       }
+      if constexpr (C::SDR)
+        if (grp == 0) {
+          const BlockDma b = blk(jlo - 1);
+          dma_ops<0, OP_R>(b, dl, junk, wave);
+          dma_ops<OP_KS, OP_V>(b, dl, junk, wave);
+        }
       if (has_sub) {
         const uint32_t ks0 = sbase + (uint32_t)(jlo % C::NKS) * C::KSLOT;
         s_tile(opaque(ks0 + C::K_OFF + ln.k), opaque(ks0 + C::R_OFF + ln.r), qf, qr, w);
       }
-      if constexpr (C::KLEAD >= 3)
+      if constexpr (C::SDR) {
+        wait_vm<0>();
+        __syncthreads();
+      } else if constexpr (C::KLEAD >= 3) {
         if (grp == 0) dma_ops<0, C::N_OPS>(blk(jlo - 1), dl, junk, wave);
+      }
 
       // Per wave the sub-tiles run as alternating half-steps X_0 G_0 X_1
       // G_1 ...: X_i is sub-tile i's softmax (vector ALU), G_i its P V and
@@ -1038,7 +1104,7 @@ struct MfmaKernel {
       using Y = std::true_type;
       using N = std::false_type;
       auto publish_block = [&]() {
-        if constexpr (C::KLEAD >= 3)
+        if constexpr (C::K_SLACK)
           publish<C::N_OPS>();  // batch j may stay in flight
         else
           publish<C::V_DMA>();  // batch j's K part must be in too
@@ -1128,12 +1194,18 @@ struct MfmaKernel {
         }
         continue;
       }
-      char* ost = smem + wave * 32 * C::O_ROW + lane32 * C::O_ROW;
+      // SDR: the staging addresses are recomputed per item, from a lane index
+      // the compiler cannot see through, instead of hoisted out of the item
+      // loop as constants that would not fit in the registers beside the
+      // loop's state
+      const int el = C::SDR ? (int)opaque((uint32_t)lane) : lane;
+      const int el32 = el & 31, ehf = el >> 5;
+      char* ost = smem + wave * 32 * C::O_ROW + el32 * C::O_ROW;
 #pragma unroll
       for (int t = 0; t < C::DV_TILES; ++t)
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-          const int dv0 = t * 32 + 8 * a4 + 4 * hf;
+          const int dv0 = t * 32 + 8 * a4 + 4 * ehf;
           const uint32_t lo = pack_bf16x2(w.o[t][4 * a4 + 0] * inv, w.o[t][4 * a4 + 1] * inv);
           const uint32_t hi = pack_bf16x2(w.o[t][4 * a4 + 2] * inv, w.o[t][4 * a4 + 3] * inv);
           *reinterpret_cast<i32x2*>(ost + dv0 * 2) = i32x2{(int)lo, (int)hi};
@@ -1144,7 +1216,7 @@ struct MfmaKernel {
       constexpr int CPR = C::DV * 2 / 16;  // 16-byte chunks per output row
 #pragma unroll
       for (int i = 0; i < 32 * CPR / kWave; ++i) {
-        const int c = lane + i * kWave;
+        const int c = el + i * kWave;
         const int r = c / CPR, cc = c % CPR;
         const int row = wq0 + r;
         if (row < L) {
