@@ -684,40 +684,6 @@ struct MfmaKernel {
           w.st[e] *= ks[8 * (e >> 2) + 4 * hf + (e & 3)];
       }
     }
-    if constexpr (C::FP8) {
-      // fp8 layouts: row max first (their half-step is longer anyway, and
-      // the max-first form measured faster there)
-      float x = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        if (MAYMASK && mask && 8 * (e >> 2) + (e & 3) > rel) w.st[e] = -INFINITY;
-        x = fmaxf(x, w.st[e]);
-      }
-      const float mx = half_max(x) * cq;
-      constexpr float kLazy = 32.f;
-      if (wave_any(mx > w.m + kLazy)) {
-        const float m_new = fmaxf(w.m, mx);
-        const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(w.m - m_new);
-        w.l *= alpha;
-#pragma unroll
-        for (int t = 0; t < C::DV_TILES; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) w.o[t][r] *= alpha;
-        w.m = m_new;
-      }
-      const float m_use = w.m == -INFINITY ? 0.f : w.m;
-      float ls[2];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        w.st[e] = fast_exp2(fmaf(w.st[e], cq, -m_use));
-        ls[e & 1] = e < 2 ? w.st[e] : ls[e & 1] + w.st[e];  // no add of the zero start
-        if (e & 1) w.pw[e >> 1] = pack_bf16x2(w.st[e - 1], w.st[e]);
-      }
-      w.l += ls[0] + ls[1];
-      (void)first;
-      MHA_SLOT_FENCE();
-      return;
-    }
     if (MAYMASK && mask) {
 #pragma unroll
       for (int e = 0; e < 16; ++e)
