@@ -876,6 +876,57 @@ struct MfmaKernel {
     QFrag qf_x[EARLY_Q ? NQF : 1];
     bf16x8 qr_x[EARLY_Q ? NQR : 1];
     float cq_x = 0.f;
+    // bf16: the early Q loads read whole rows (RPI rows of QRB bytes per
+    // instruction, a few cache lines each, instead of one 16-byte piece of
+    // each of 32 rows) into the fragment registers themselves, and the rows
+    // are rearranged into the
+    // fragment layout through this wave's 32 QRB-byte part of the V ring,
+    // which is idle between two items (chunk c of row r at chunk position
+    // c ^ (r % QCPR), so that neither the writes nor the fragment reads
+    // meet on a bank)
+    constexpr bool QROWS = EARLY_Q && !C::FP8;
+    constexpr int QRB = C::DN * 2, QCPR = QRB / 16, QRPI = kWave / QCPR;
+    static_assert(!QROWS || (32 / QRPI == C::QK_STEPS && 8 * 32 * QRB <= C::NVS * C::VSLOT),
+                  "a wave's Q rows fit its part of the V ring, one instruction per step");
+    const uint32_t qarea = sbase + C::V_BASE + (uint32_t)wave * (32 * QRB);
+    // (the per-lane offsets are recomputed at each call, from a lane index
+    // the compiler cannot see through, rather than kept in registers across
+    // the block loop)
+    auto load_q_rows = [&](const WorkItem& nw) {
+      const int r0 = nw.qt * C::BM + wave * 32;
+      const int ql = (int)opaque((uint32_t)lane);
+#pragma unroll
+      for (int i = 0; i < C::QK_STEPS; ++i) {
+        const int r = QRPI * i + ql / QCPR, c = ql % QCPR;
+        i32x4 x = {0, 0, 0, 0};
+        if (r0 + r < nw.L)
+          x = *reinterpret_cast<const i32x4*>(
+              qp + (((size_t)(nw.s0 + r0 + r) * p.num_heads + nw.h) * C::DN) * 2 + c * 16);
+        if constexpr (QROWS) qf_x[i] = __builtin_bit_cast(bf16x8, x);
+      }
+      cq_x = p.scale_log2;
+      if (!(cq_x >= 1.17549435e-38f)) cq_x = 1.17549435e-38f;
+    };
+    auto place_q_rows = [&]() {
+      typedef __attribute__((address_space(3))) i32x4 li32x4;
+      const int ql = (int)opaque((uint32_t)lane);
+      const int ql32 = ql & 31, qhf = ql >> 5;
+      const uint32_t qa = opaque(qarea);
+#pragma unroll
+      for (int i = 0; i < C::QK_STEPS; ++i) {
+        const int r = QRPI * i + ql / QCPR, c = ql % QCPR;
+        if constexpr (QROWS)
+          *reinterpret_cast<li32x4*>(const_cast<lchar*>(
+              lp(qa + r * QRB + 16 * (c ^ (r % QCPR))))) = __builtin_bit_cast(i32x4, qf_x[i]);
+      }
+      if constexpr (QROWS) {
+#pragma unroll
+        for (int s = 0; s < C::QK_STEPS; ++s)
+          qf_x[s] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const li32x4*>(
+                          lp(qa + ql32 * QRB + 16 * ((2 * s + qhf) ^ (ql32 % QCPR)))));
+      }
+    };
     for (int it = 0;; ++it) {
       __syncthreads();
       // the item is the same for the whole workgroup: keep it in SGPRs
@@ -1133,7 +1184,12 @@ struct MfmaKernel {
                               __builtin_amdgcn_readfirstlane(s_item[(it + 1) & 1][1]),
                               __builtin_amdgcn_readfirstlane(s_item[(it + 1) & 1][2]),
                               __builtin_amdgcn_readfirstlane(s_item[(it + 1) & 1][3])});
-        if (nw.L >= 0) load_q(nw, qf_x, qr_x, cq_x);
+        if (nw.L >= 0) {
+          if constexpr (QROWS)
+            load_q_rows(nw);
+          else
+            load_q(nw, qf_x, qr_x, cq_x);
+        }
       }
 
       // ---- epilogue
@@ -1158,6 +1214,7 @@ struct MfmaKernel {
             p.lse_part[((size_t)wi.split * p.num_heads + wi.h) * p.part_tokens + s0 + qi] =
                 lt > 0.f ? (w.m + log2f(lt)) * kLn2 : -INFINITY;
         }
+        if constexpr (QROWS) place_q_rows();
         continue;
       }
       // SDR: the staging addresses are recomputed per item, from a lane index
@@ -1192,6 +1249,7 @@ struct MfmaKernel {
                                     cc * 16) = x;
         }
       }
+      if constexpr (QROWS) place_q_rows();
     }
   }
 };
