@@ -1,12 +1,15 @@
 """Throughput of the fused attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--settle-s SECONDS] [--no-cpu-baseline]
 
 A step is one mha_fwd call (scheduler prepass + attention kernel; with
 --splits N > 1 also the split merge) over the whole workload, inputs
 resident in HBM.  Default workload: bf16 causal
-prefill, B=4, H=32, S=4096, D=128.  Prints one JSON line.
+prefill, B=4, H=32, S=4096, D=128.  Prints one JSON line.  Before the W
+warm-up steps, untimed steps run for --settle-s seconds (default 0.3), so
+that the part has reached its steady speed; the JSON line reports them
+under "settle".
 
 value      attention TFLOP/s = metric FLOPs (4*B*H*S^2*D, halved for causal)
            / mean step time over the K timed steps;
@@ -137,6 +140,8 @@ class HipEvents:
         self.hip.hipEventDestroy(ev)
 
 
+
+
 def peak_for(inp, fast_accum: bool = False) -> float:
     # fp8 codes decoded to bfloat16 (the default) run every product at the
     # bf16 rate
@@ -148,6 +153,30 @@ def peak_for(inp, fast_accum: bool = False) -> float:
     if inp.dtype == "fp8":
         return PEAK_TFLOPS["bf16"]
     return PEAK_TFLOPS[inp.dtype]
+
+
+def settle_clocks(step, seconds: float):
+    """Run `step` untimed until `seconds` of wall time have passed, before
+    the warm-up steps.  From a fresh process the part needs about a hundred
+    launches of sustained load to reach its steady speed: on the causal B4
+    H32 S4096 workload, 20 instrumented steps after 5 warm-up steps averaged
+    584 us (664 us falling to 531 us), and 495 us after 300 untimed steps,
+    so a few warm-up steps alone would time the ramp, not the kernel.
+    Returns (steps, seconds)."""
+    import torch
+    n, t0, marks = 0, time.perf_counter(), []
+    while True:
+        for _ in range(8):
+            step()
+        n += 8
+        # keep two chunks of steps queued, so that the device never idles
+        marks.append(torch.cuda.Event())
+        marks[-1].record()
+        if len(marks) > 2:
+            marks.pop(0).synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            torch.cuda.synchronize()
+            return n, time.perf_counter() - t0
 
 
 def cpu_model() -> str:
@@ -368,13 +397,17 @@ def bench_quantize(a, lib, dev) -> int:
     scales = torch.empty((T, H), dtype=torch.float32, device=dev)
     rows = T * H
     nbytes = rows * D * 2 + rows * D + rows * 4  # read x, write codes and scales
-    for _ in range(a.warmup):
-        mha_quantize_fp8(x, codes=codes, scales=scales)
-    torch.cuda.synchronize()
     # kernel-only durations: the library records these HIP events right
     # before and after its launch (mha_fwd_set_kernel_events)
     hip = HipEvents()
     kev = [(hip.create(), hip.create()) for _ in range(a.steps)]
+    settle = None
+    if a.settle_s > 0:
+        n, dt = settle_clocks(lambda: mha_quantize_fp8(x, codes=codes, scales=scales), a.settle_s)
+        settle = {"steps": n, "seconds": round(dt, 3)}
+    for _ in range(a.warmup):
+        mha_quantize_fp8(x, codes=codes, scales=scales)
+    torch.cuda.synchronize()
     for e0, e1 in kev:
         _native.check(lib.mha_fwd_set_kernel_events(e0, e1))
         mha_quantize_fp8(x, codes=codes, scales=scales)
@@ -419,6 +452,7 @@ def bench_quantize(a, lib, dev) -> int:
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": cpu,
+        "settle": settle,
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -429,6 +463,9 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="untimed steps for this many seconds before the warm-up steps, so "
+                         "that the part reaches its steady speed (0: none)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=mi.WORKLOAD_ORDER + list(mi.EXTRA_WORKLOADS))
     ap.add_argument("--splits", type=int, default=1,
@@ -512,18 +549,21 @@ def main(argv=None):
                 q_rope=qr, k_rope=kr, q_scale=qs, k_scale=ks,
                 softmax_scale=inp.softmax_scale, out=o, lse=lse, fp8_fast_accum=fast, **part)
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    if not (bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())):
-        print("[bench] non-finite output", file=sys.stderr)
-        return 1
-
+    # everything the timed region needs is set up first, so that nothing but
+    # launches runs between the settling, the warm-up and the timed steps
     hip = HipEvents()
     kev = [(hip.create(), hip.create()) for _ in range(a.steps)]
     stream = torch.cuda.current_stream(dev)
     t_all0 = torch.cuda.Event(enable_timing=True)
     t_all1 = torch.cuda.Event(enable_timing=True)
+    settle = None
+    if a.settle_s > 0:
+        n, dt = settle_clocks(step, a.settle_s)
+        settle = {"steps": n, "seconds": round(dt, 3)}
+        print(f"[bench] clocks settled: {n} untimed steps in {dt:.2f} s", file=sys.stderr,
+              flush=True)
+    for _ in range(a.warmup):
+        step()
     torch.cuda.synchronize()
     t_all0.record(stream)
     for i in range(a.steps):
@@ -539,6 +579,9 @@ def main(argv=None):
         hip.destroy(s1)
     ms_per_step = total_ms / a.steps
     kmean = float(np.mean(kernel_ms))
+    if not (bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())):
+        print("[bench] non-finite output", file=sys.stderr)
+        return 1
 
     flops = mi.attention_flops(inp)
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -548,6 +591,8 @@ def main(argv=None):
     print(f"[bench] {ms_per_step * 1e3:.1f} us/step, attention kernel mean {kmean * 1e3:.1f} us "
           f"(min {min(kernel_ms) * 1e3:.1f}), {value:.1f} TFLOP/s, {100 * achieved / peak:.1f}% "
           f"of {peak:.0f}", file=sys.stderr, flush=True)
+    print("[bench] attention kernel per timed step (us): "
+          + " ".join(f"{x * 1e3:.0f}" for x in kernel_ms), file=sys.stderr, flush=True)
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -592,6 +637,7 @@ def main(argv=None):
             "traffic": None if traffic is None else round(traffic),
         },
         "cpu_baseline": cpu,
+        "settle": settle,
     }
     print(json.dumps(line), flush=True)
     return 0
