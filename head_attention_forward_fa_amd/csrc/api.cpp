@@ -307,7 +307,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   auto* table = reinterpret_cast<mha::i32x4*>(ws + kStateBytes);
   auto* gwork = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
 
-  const int chunk = mha::prepass_chunk(causal, num_heads / num_kv_heads);
+  const int chunk = mha::prepass_chunk(causal, num_heads / num_kv_heads,
+                                       (max_seqlen + var->block_m - 1) / var->block_m);
   e = mha::launch_prepass(cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads, causal,
                           var->block_m, var->block_n, num_splits, plan.capacity, chunk, table, st,
                           gwork, s);
@@ -493,7 +494,8 @@ int mha_sched_visit(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen
   auto* st = reinterpret_cast<mha::SchedState*>(ws);
   auto* table = reinterpret_cast<mha::i32x4*>(ws + kStateBytes);
   auto* gwork = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
-  const int chunk = mha::prepass_chunk(causal, num_heads / num_kv_heads);
+  const int chunk = mha::prepass_chunk(causal, num_heads / num_kv_heads,
+                                       (max_seqlen + block_m - 1) / block_m);
   e = mha::launch_prepass(cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads, causal, block_m,
                           block_n, 1, plan.capacity, chunk, table, st, gwork, s);
   if (e != hipSuccess) return fail_hip(e, "scheduler prepass launch");
