@@ -306,7 +306,7 @@ int mha_combine_splits(const float* o_partial, const float* lse_partial, int32_t
  * sequence taken at max_seqlen, nb = ceil(max_seqlen / 64) key blocks for
  * the longest work item and W = the blocks of all items (causal: q-tile t of
  * 256 rows sees min(nb, 4 (t + 1)) blocks) over `cus` compute units: 1 when
- * 4 nb <= 5 ceil(W / cus), else ceil(2 nb / ceil(W / cus)) capped at 8 and at
+ * 4 nb <= 5 ceil(W / cus), else ceil(1.2 nb / ceil(W / cus)) capped at 8 and at
  * nb / 8 (at least 8 blocks per split), lowered until the float32 partials
  * (splits x batch x max_seqlen x num_heads x v_dim x 4 bytes) fit in 1 GiB.
  * The split (SM100AttentionSMem, comptime members: MiscMBarsType takes the

@@ -172,8 +172,9 @@ def test_auto_splits_rule():
     assert auto(2, 8192, 16, True, 128, cus) == 1
     assert auto(1, 16384, 4, False, 128, cus) == 1       # one full-length item per CU
     # one causal sequence, 4 heads: 256 items, the longest 256 blocks against
-    # 130 blocks of work per CU: splits of about half of that
-    assert auto(1, 16384, 4, True, 128, cus) == 4
+    # 130 blocks of work per CU: ceil(1.2 x 256 / 130) splits
+    assert auto(1, 16384, 4, True, 128, cus) == 3
+    assert auto(1, 16384, 2, True, 128, cus) == 5         # 65 blocks per CU
     assert auto(1, 2048, 2, True, 128, cus) == 4         # capped at 8 blocks per split
     assert auto(1, 960, 2, True, 128, cus) == 1          # fewer than 16 key blocks
     assert auto(1, 1024, 2, True, 128, cus) == 2
