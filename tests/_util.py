@@ -94,8 +94,10 @@ def oracle_rows(inp: Inputs, tokens):
     return o, lse
 
 
-def sample_tokens(inp: Inputs, n_random: int = 24, seed: int = 1):
-    """First, last and tile-boundary rows of every sequence plus random ones."""
+def sample_tokens(inp: Inputs, n_random: int = 256, seed: int = 1):
+    """First, last and tile-boundary rows of every sequence (the first and
+    last row of every 256-row query tile, so that a work item that wrote the
+    wrong tile or not at all shows), plus random ones."""
     cu = inp.cu_seqlens.astype(np.int64)
     rng = np.random.default_rng(seed)
     toks = set()
@@ -107,6 +109,9 @@ def sample_tokens(inp: Inputs, n_random: int = 24, seed: int = 1):
                   s1 - s0 - 2, s1 - s0 - 1):
             if 0 <= i < s1 - s0:
                 toks.add(s0 + i)
+        for t0 in range(0, s1 - s0, 256):
+            toks.add(s0 + t0)
+            toks.add(s0 + min(t0 + 255, s1 - s0 - 1))
     if inp.total_tokens:
         toks.update(int(x) for x in rng.integers(0, inp.total_tokens, n_random))
     return np.array(sorted(toks), dtype=np.int64)

@@ -1,7 +1,7 @@
 """HIP path vs the float64 oracle, element by element, through the C ABI.
 
 Small cases (seconds for the oracle) span several 256-row query tiles and
-64-key blocks (enough of them to wrap the kernel's 4-slot K and 3-slot V rings) with ragged tails, GQA, empty sequences, the nope/rope split and
+64-key blocks (enough of them to wrap the kernel's K and V rings) with ragged tails, GQA, empty sequences, the nope/rope split and
 fp8; the five named workloads run at full size with the oracle evaluated on
 sampled rows (first, last, tile-boundary and random tokens, every head).
 Tolerances (max-abs): O 1e-4 fp32, 2e-2 bf16, 6e-2 fp8; LSE 1e-3.
