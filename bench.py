@@ -272,6 +272,7 @@ def summarize_profile(prof: str, workload: str) -> str:
     stats = _csv_rows(os.path.join(prof, "trace"), "kernel_stats.csv")
     krow = next(r for r in stats if KERNEL in r["Name"])
     prow = [r for r in stats if "sched_prepass" in r["Name"]]
+    crow = [r for r in stats if "combine_splits" in r["Name"]]  # split-KV merge
     avg_ns = float(krow["AverageNs"])
     a = _pmc_per_dispatch(os.path.join(prof, "pmcA"), KERNEL)
     b = _pmc_per_dispatch(os.path.join(prof, "pmcB"), KERNEL)
@@ -321,13 +322,21 @@ def summarize_profile(prof: str, workload: str) -> str:
         "|---|---|---|---|---|",
         f"| {KERNEL} | {krow['Calls']} | {avg_ns:.0f} | {krow['MinNs']} | {krow['MaxNs']} |",
     ]
-    for r in prow:
-        lines.append(f"| sched_prepass_kernel | {r['Calls']} | {float(r['AverageNs']):.0f} | "
-                     f"{r['MinNs']} | {r['MaxNs']} |")
+    for name, rows in (("sched_prepass_kernel", prow), ("combine_splits_kernel", crow)):
+        for r in rows:
+            lines.append(f"| {name} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
+                         f"{r['MinNs']} | {r['MaxNs']} |")
     lines += [
         "",
         f"Attention TFLOP/s at the trace average: {flops / (avg_ns * 1e-9) / 1e12:.1f} "
         f"({100 * flops / (avg_ns * 1e-9) / 1e12 / peak:.1f}% of {peak:.0f}).",
+    ]
+    if crow:
+        step_ns = avg_ns + sum(float(r["AverageNs"]) for r in prow + crow)
+        lines.append(f"With the key splits' merge and the prepass (trace averages, no launch "
+                     f"gaps): {step_ns / 1e3:.1f} us, {flops / (step_ns * 1e-9) / 1e12:.1f} "
+                     f"TFLOP/s.")
+    lines += [
         "",
         "## Counters (per dispatch of the attention kernel, mean)",
         "",
