@@ -940,7 +940,12 @@ struct MfmaKernel {
       const int g = wi.h / p.group;
       const int q0 = wi.qt * C::BM;    // first query row of the tile
       const int wq0 = q0 + wave * 32;  // first query row of this wave
-      const int qi = wq0 + lane32;     // this lane's query row
+      // (fast fp8 with a rope part: the lane-derived values of an item come
+      // from a lane index the compiler cannot see through, so that they are
+      // recomputed per item instead of kept, and spilled, across the loop)
+      constexpr bool OPQ = C::MIXED && C::F8MMA;
+      const int ol = OPQ ? (int)opaque((uint32_t)lane) : 0;
+      const int qi = wq0 + (OPQ ? (ol & 31) : lane32);  // this lane's query row
       const bool qvalid = qi < L;
       const size_t qrow = (size_t)(s0 + qi) * p.num_heads + wi.h;
 
@@ -980,20 +985,20 @@ struct MfmaKernel {
               i32x4 x = {0, 0, 0, 0};
               if (qvalid)
                 x = *reinterpret_cast<const i32x4*>(
-                    qrp + (qrow * C::DR + (s - C::QK_STEPS) * 16 + 8 * hf) * 2);
+                    qrp + (qrow * C::DR + (s - C::QK_STEPS) * 16 + 8 * (OPQ ? (ol >> 5) : hf)) * 2);
               qr_i[s - C::QK_STEPS] = __builtin_bit_cast(bf16x8, x);
               continue;
             }
           }
           if constexpr (C::FP8 && !C::F8MMA) {
             i32x2 x = {0, 0};
-            if (qvalid) x = *reinterpret_cast<const i32x2*>(qp + qrow * C::DN + s * 16 + 8 * hf);
+            if (qvalid) x = *reinterpret_cast<const i32x2*>(qp + qrow * C::DN + s * 16 + 8 * (OPQ ? (ol >> 5) : hf));
             qf_i[s] = dec8(x);
           } else if constexpr (C::FP8) {
             i32x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
             if (qvalid) {
               const i32x4* src =
-                  reinterpret_cast<const i32x4*>(qp + qrow * C::DN + s * 64 + 32 * hf);
+                  reinterpret_cast<const i32x4*>(qp + qrow * C::DN + s * 64 + 32 * (OPQ ? (ol >> 5) : hf));
               const i32x4 a0 = src[0], a1 = src[1];
               x = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             }
@@ -1002,8 +1007,8 @@ struct MfmaKernel {
             i32x4 x = {0, 0, 0, 0};
             if (qvalid) {
               const char* src = s < C::QK_STEPS
-                                    ? qp + (qrow * C::DN + s * 16 + 8 * hf) * 2
-                                    : qrp + (qrow * C::DR + (s - C::QK_STEPS) * 16 + 8 * hf) * 2;
+                                    ? qp + (qrow * C::DN + s * 16 + 8 * (OPQ ? (ol >> 5) : hf)) * 2
+                                    : qrp + (qrow * C::DR + (s - C::QK_STEPS) * 16 + 8 * (OPQ ? (ol >> 5) : hf)) * 2;
               x = *reinterpret_cast<const i32x4*>(src);
             }
             qf_i[s] = __builtin_bit_cast(bf16x8, x);
@@ -1096,8 +1101,9 @@ struct MfmaKernel {
         const float* ks =
             reinterpret_cast<const float*>(smem + (j % C::NKS) * C::KSLOT + C::KS_OFF) + 32 * H;
         if (!CHK || i < n_sub)
-          xphase<O0, O1, CHK>(w, i == 2 * jlo, ks, hf, cq, p.scale_log2,
-                              SPLIT ? i == last_sub : i == n_sub - 1, lim - 32 * i - 4 * hf, bd,
+          xphase<O0, O1, CHK>(w, i == 2 * jlo, ks, OPQ ? (ol >> 5) : hf, cq, p.scale_log2,
+                              SPLIT ? i == last_sub : i == n_sub - 1,
+                              lim - 32 * i - 4 * (OPQ ? (ol >> 5) : hf), bd,
                               dl, junk, wave);
         else
           dma_ops<O0, O1>(bd, dl, junk, wave);
@@ -1199,8 +1205,11 @@ struct MfmaKernel {
         // split-KV partial: float32 O over this item's key range (zero where
         // the range holds no visible key) and its LSE (-inf there), straight
         // from the registers: each lane writes 16-byte runs of its row
-        if (qvalid && s0 + qi < p.part_tokens) {
-          const size_t prow = ((size_t)wi.split * p.part_tokens + s0 + qi) * p.num_heads + wi.h;
+        const int sl = OPQ ? (int)opaque((uint32_t)lane) : 0;
+        if ((OPQ ? wq0 + (sl & 31) < L : qvalid) &&
+            s0 + (OPQ ? wq0 + (sl & 31) : qi) < p.part_tokens) {
+          const size_t prow = ((size_t)wi.split * p.part_tokens + s0 +
+                               (OPQ ? wq0 + (sl & 31) : qi)) * p.num_heads + wi.h;
           float* dst = p.o_part + prow * C::DV;
 #pragma unroll
           for (int t = 0; t < C::DV_TILES; ++t)
@@ -1208,10 +1217,11 @@ struct MfmaKernel {
             for (int a4 = 0; a4 < 4; ++a4) {
               const f32x4 x = {w.o[t][4 * a4 + 0] * inv, w.o[t][4 * a4 + 1] * inv,
                                w.o[t][4 * a4 + 2] * inv, w.o[t][4 * a4 + 3] * inv};
-              *reinterpret_cast<f32x4*>(dst + t * 32 + 8 * a4 + 4 * hf) = x;
+              *reinterpret_cast<f32x4*>(dst + t * 32 + 8 * a4 + 4 * (OPQ ? sl >> 5 : hf)) = x;
             }
-          if (hf == 0)
-            p.lse_part[((size_t)wi.split * p.num_heads + wi.h) * p.part_tokens + s0 + qi] =
+          if ((OPQ ? sl >> 5 : hf) == 0)
+            p.lse_part[((size_t)wi.split * p.num_heads + wi.h) * p.part_tokens + s0 +
+                       (OPQ ? wq0 + (sl & 31) : qi)] =
                 lt > 0.f ? (w.m + log2f(lt)) * kLn2 : -INFINITY;
         }
         if constexpr (QROWS) place_q_rows();
@@ -1221,7 +1231,7 @@ struct MfmaKernel {
       // the compiler cannot see through, instead of hoisted out of the item
       // loop as constants that would not fit in the registers beside the
       // loop's state
-      const int el = C::SDR ? (int)opaque((uint32_t)lane) : lane;
+      const int el = C::SDR || OPQ ? (int)opaque((uint32_t)lane) : lane;
       const int el32 = el & 31, ehf = el >> 5;
       char* ost = smem + wave * 32 * C::O_ROW + el32 * C::O_ROW;
 #pragma unroll
@@ -1233,8 +1243,9 @@ struct MfmaKernel {
           const uint32_t hi = pack_bf16x2(w.o[t][4 * a4 + 2] * inv, w.o[t][4 * a4 + 3] * inv);
           *reinterpret_cast<i32x2*>(ost + dv0 * 2) = i32x2{(int)lo, (int)hi};
         }
-      if (hf == 0 && qvalid)
-        p.lse[(size_t)wi.h * T + s0 + qi] = lt > 0.f ? (w.m + log2f(lt)) * kLn2 : -INFINITY;
+      if (OPQ ? ehf == 0 && wq0 + el32 < L : hf == 0 && qvalid)
+        p.lse[(size_t)wi.h * T + s0 + (OPQ ? wq0 + el32 : qi)] =
+            lt > 0.f ? (w.m + log2f(lt)) * kLn2 : -INFINITY;
       __syncthreads();
       constexpr int CPR = C::DV * 2 / 16;  // 16-byte chunks per output row
 #pragma unroll
