@@ -132,6 +132,10 @@ struct Plan {
   size_t bytes;  // workspace size
 };
 
+// float32 calls with at most this many sequences (and at most one work item
+// per workgroup of a full launch) skip the scheduler: see `direct` below
+constexpr int kDirectMaxBatch = 64;
+
 int make_plan(int batch, int max_seqlen, int num_heads, int num_kv_heads, int block_m,
               int num_splits, Plan* plan) {
   long long tiles = ((long long)max_seqlen + block_m - 1) / block_m;
@@ -287,8 +291,17 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
 
   const float sigma =
       softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)(head_dim_nope + head_dim_rope));
+  // float32 problems small enough for one workgroup per work item (the
+  // (sequence, head, q-tile) grid of max_seqlen) map item = workgroup
+  // directly: no work table, no prepass launch, no queue round trips (the
+  // kernel reads cu_seqlens, and refuses lengths as the prepass would)
+  const long long full_grid = (long long)cu_count(dev) * var->blocks_per_cu();
+  const bool direct = dtype == MHA_DTYPE_F32 && num_splits == 1 && !split_here &&
+                      plan.capacity <= full_grid && batch <= kDirectMaxBatch;
   char* ws = nullptr;
-  if (noalloc) {
+  if (direct) {
+    // (nothing to stage)
+  } else if (noalloc) {
     if (plan.bytes > kNoAllocBytes)
       return fail(MHA_ERR_INVALID_ARG,
                   "mha_fwd_noalloc: the work table needs " + std::to_string(plan.bytes) +
@@ -299,22 +312,24 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
     e = get_workspace(dev, s, plan.bytes + part_bytes, &ws);
     if (e != hipSuccess) return fail_hip(e, "workspace allocation");
   }
-  if (split_here) {
+  if (split_here && !direct) {
     o_part = reinterpret_cast<float*>(ws + plan.bytes);
     lse_part = reinterpret_cast<float*>(
         ws + plan.bytes +
         align_up((size_t)num_splits * total_tokens * num_heads * v_dim * sizeof(float), 256));
   }
-  auto* st = reinterpret_cast<mha::SchedState*>(ws);
-  auto* table = reinterpret_cast<mha::i32x4*>(ws + kStateBytes);
-  auto* gwork = reinterpret_cast<int*>(ws + kStateBytes + align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
-
-  const int chunk = mha::prepass_chunk(causal, num_heads / num_kv_heads,
-                                       (max_seqlen + var->block_m - 1) / var->block_m);
-  e = mha::launch_prepass(cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads, causal,
-                          var->block_m, var->block_n, num_splits, plan.capacity, chunk, table, st,
-                          gwork, s);
-  if (e != hipSuccess) return fail_hip(e, "scheduler prepass launch");
+  auto* st = direct ? nullptr : reinterpret_cast<mha::SchedState*>(ws);
+  auto* table = direct ? nullptr : reinterpret_cast<mha::i32x4*>(ws + kStateBytes);
+  if (!direct) {
+    auto* gwork = reinterpret_cast<int*>(ws + kStateBytes +
+                                         align_up((size_t)plan.capacity * sizeof(mha::i32x4), 256));
+    const int chunk = mha::prepass_chunk(causal, num_heads / num_kv_heads,
+                                         (max_seqlen + var->block_m - 1) / var->block_m);
+    e = mha::launch_prepass(cu_seqlens, batch, max_seqlen, num_heads, num_kv_heads, causal,
+                            var->block_m, var->block_n, num_splits, plan.capacity, chunk, table,
+                            st, gwork, s);
+    if (e != hipSuccess) return fail_hip(e, "scheduler prepass launch");
+  }
 
   mha::AttnParams p;
   p.q = q;
@@ -339,16 +354,22 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   p.part_tokens = total_tokens;
   p.o_part = num_splits > 1 ? o_part : nullptr;
   p.lse_part = num_splits > 1 ? lse_part : nullptr;
+  p.max_seqlen = max_seqlen;
 
-  long long grid = (long long)cu_count(dev) * var->blocks_per_cu();
-  if (grid > plan.capacity) grid = plan.capacity;
-  if (grid < 1) grid = 1;
+  // direct: exactly one workgroup per item of the grid (none when
+  // max_seqlen is 0: every sequence is then empty or the call is refused,
+  // and either way nothing is written)
+  long long grid = direct ? plan.capacity : full_grid;
+  if (!direct && grid > plan.capacity) grid = plan.capacity;
+  if (!direct && grid < 1) grid = 1;
   if (g_ev_start) {
     e = hipEventRecord(g_ev_start, s);
     if (e != hipSuccess) return fail_hip(e, "hipEventRecord (start)");
   }
-  e = (num_splits > 1 ? var->launch_split : var->launch)(p, (int)grid, s);
-  if (e != hipSuccess) return fail_hip(e, "attention kernel launch");
+  if (grid > 0) {
+    e = (num_splits > 1 ? var->launch_split : var->launch)(p, (int)grid, s);
+    if (e != hipSuccess) return fail_hip(e, "attention kernel launch");
+  }
   if (g_ev_stop) {
     e = hipEventRecord(g_ev_stop, s);
     if (e != hipSuccess) return fail_hip(e, "hipEventRecord (stop)");

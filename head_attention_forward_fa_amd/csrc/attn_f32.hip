@@ -71,11 +71,33 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
   // wave 0 runs the work-item source: the next item is reserved when an
   // item starts and its entry read after the wave's key blocks, so neither
   // round trip delays the wave's products; the entry is published at the
-  // end of the current item
+  // end of the current item.  Without a table (direct mapping, small
+  // problems) the workgroup's only item is item blockIdx.x of the
+  // (sequence, head, q-tile) grid the launch covers, read from cu_seqlens
+  // here; a length below 0 or above max_seqlen refuses the call in every
+  // workgroup, as the prepass does.
+  const bool direct = p.table == nullptr;
   Fetcher fetch;
   if (wave == 0) {
-    fetch.init(p.sched);
-    const i32x4 e0 = fetch.resolve(p.sched, p.table);
+    i32x4 e0 = {0, -1, 0, 0};
+    if (direct) {
+      bool bad = false;
+      for (int b = lane; b < p.batch; b += kWave) {
+        const int Lb = p.cu_seqlens[b + 1] - p.cu_seqlens[b];
+        bad = bad || Lb < 0 || Lb > p.max_seqlen;
+      }
+      const int tiles = (p.max_seqlen + BM - 1) / BM;
+      const int idx = (int)blockIdx.x;
+      const int qt = idx % tiles, bh = idx / tiles;
+      const int h = bh % H, b = bh / H;
+      if (!wave_any(bad) && b < p.batch) {
+        const int s0 = p.cu_seqlens[b], Lb = p.cu_seqlens[b + 1] - s0;
+        if (qt * BM < Lb) e0 = i32x4{s0, Lb, (h << 20) | qt, b};
+      }
+    } else {
+      fetch.init(p.sched);
+      e0 = fetch.resolve(p.sched, p.table);
+    }
     if (lane == 0) s_item[0] = e0;
   }
   for (int it = 0;; ++it) {
@@ -85,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
                                          __builtin_amdgcn_readfirstlane(s_item[it & 1][2]),
                                          __builtin_amdgcn_readfirstlane(s_item[it & 1][3])});
     if (w.L < 0) break;
-    if (wave == 0) fetch.reserve(p.sched);
+    if (wave == 0 && !direct) fetch.reserve(p.sched);
     const int s0 = w.s0, L = w.L;
     const int g = w.h / p.group;
     const int q0 = w.qt * BM;
@@ -189,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(AttnParams p) {
     }
 
     i32x4 nxt = {0, -1, 0, 0};
-    if (wave == 0) nxt = fetch.resolve(p.sched, p.table);
+    if (wave == 0 && !direct) nxt = fetch.resolve(p.sched, p.table);
 
     // merge the four waves' partial results: O = sum_w 2^(m_w - M) O_w /
     // sum_w 2^(m_w - M) l_w, M = max_w m_w

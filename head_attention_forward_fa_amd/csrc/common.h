@@ -86,6 +86,7 @@ struct AttnParams {
   int part_tokens;    // T of the partial layouts (rows past it are not written)
   float* o_part;
   float* lse_part;
+  int max_seqlen;     // the caller's bound on every sequence length
 };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -132,6 +132,11 @@ typedef enum {
  * float32 rounding of the merge.  Never with fewer than 16 key blocks
  * (max_seqlen <= 960).
  *
+ * Small float32 calls (batch <= 64, and no more (sequence, head, q-tile)
+ * items of the max_seqlen grid than one full launch has workgroups) skip the
+ * scheduler: workgroup i takes item i directly, with no prepass launch and
+ * no workspace; the refusal above holds the same.
+ *
  * The library owns a workspace per (device, stream): the work table and
  * queue counters of the persistent scheduler, and the partials of its own
  * key splits.  It is allocated on the first call for that pair (so the first

@@ -189,14 +189,18 @@ def test_all_sequences_empty_and_zero_max_seqlen():
     assert o.shape == (0, 2, 128) and lse.shape == (2, 0)
 
 
-def test_overflowing_lengths_are_refused_without_writes():
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_overflowing_lengths_are_refused_without_writes(dt):
     # max_seqlen 128 sizes the table for one tile per (sequence, head); a
     # 300-token sequence needs two, so the device refuses and writes nothing
+    # (f32: a problem this small takes the direct item mapping, whose
+    # workgroups check the lengths themselves)
     from head_attention_forward_fa_amd import mha_fwd
-    inp = mi.make_inputs(dtype="bf16", seqlens=[300], num_heads=2, num_kv_heads=2,
+    inp = mi.make_inputs(dtype=dt, seqlens=[300], num_heads=2, num_kv_heads=2,
                          head_dim_nope=128, v_dim=128, causal=True, seed=5)
     t = device_tensors(inp)
-    out = torch.full((300, 2, 128), 7.0, dtype=torch.bfloat16, device="cuda:0")
+    out = torch.full((300, 2, 128), 7.0,
+                     dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device="cuda:0")
     lse = torch.full((2, 300), 7.0, dtype=torch.float32, device="cuda:0")
     mha_fwd(t["q"], t["k"], t["v"], causal=True, cu_seqlens=t["cu_seqlens"], max_seqlen=128,
             out=out, lse=lse)
