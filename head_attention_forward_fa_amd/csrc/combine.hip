@@ -54,14 +54,24 @@ __global__ __launch_bounds__(kCombineThreads) void combine_splits_kernel(
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float total = 0.f;
   if (m > -INFINITY) {
+    // four partials' loads in flight at a time; an empty partial (LSE -inf)
+    // is loaded too but selected away, so whatever it holds adds nothing
     const float* op = o_part + (size_t)row * DV + 4 * c;
-    for (int sp = 0; sp < num_splits; ++sp) {
-      const float ls = lp[sp * split_stride_l];
-      const float wgt = ls > -INFINITY ? __expf(ls - m) : 0.f;
-      total += wgt;
-      if (wgt > 0.f) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(op + sp * split_stride_o);
-        acc += wgt * x;
+    for (int sp0 = 0; sp0 < num_splits; sp0 += 4) {
+      f32x4 x[4];
+      float wgt[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sp = sp0 + u;
+        x[u] = sp < num_splits ? *reinterpret_cast<const f32x4*>(op + sp * split_stride_o)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+        const float ls = sp < num_splits ? lp[sp * split_stride_l] : -INFINITY;
+        wgt[u] = ls > -INFINITY ? __expf(ls - m) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        total += wgt[u];
+        if (wgt[u] > 0.f) acc += wgt[u] * x[u];
       }
     }
   }
