@@ -9,7 +9,9 @@
 //                                     row of zeros)
 //   code  = round-to-nearest-even E4M3 of clamp(x / scale, -448, 448)
 //
-// with IEEE float32 division, so the codes are exact functions of the input.
+// with IEEE float32 division, so the codes are exact functions of the input
+// (computed as a reciprocal product where that provably rounds the same way,
+// see the kernel).
 //
 // HBM-bound: each row is read once (D bf16 or float32 elements) and written
 // once (D codes + 4 bytes of scale).  A row is spread over LPR lanes (8
@@ -30,8 +32,8 @@ namespace {
 constexpr float kE4M3Max = 448.0f;
 constexpr int kQuantThreads = 256;
 
-// Two float32 values already inside [-448, 448] -> two E4M3 codes in the low
-// 16 bits (first value in the low byte): v_cvt_pk_fp8_f32, round to nearest
+// Two float32 values of magnitude below 464 -> two E4M3 codes in the low 16
+// bits (first value in the low byte): v_cvt_pk_fp8_f32, round to nearest
 // even, OCP E4M3 on gfx950.
 __device__ __forceinline__ uint32_t cvt2(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
@@ -57,50 +59,83 @@ __device__ __forceinline__ void load8(const void* x, size_t elem, float (&v)[8])
   }
 }
 
-// LPR lanes per row (a power of two, LPR * 8 >= cols); 256 / LPR rows per
-// workgroup.
-template <bool BF16, int LPR>
+// LPR lanes per row (a power of two, LPR * 8 >= cols); each group of LPR
+// lanes takes NR rows, NR x 256 / LPR rows per workgroup, and issues the NR
+// rows' loads before any arithmetic, so that more bytes are in flight per
+// lane than one load's worth.
+template <bool BF16, int LPR, int NR>
 __global__ __launch_bounds__(kQuantThreads) void fp8_quant_rows_kernel(const void* __restrict__ x,
                                                                       int64_t rows, int cols,
                                                                       uint8_t* __restrict__ codes,
                                                                       float* __restrict__ scales) {
-  constexpr int RPB = kQuantThreads / LPR;
-  const int c = threadIdx.x % LPR;  // 8-element chunk of the row
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  const bool live = row < rows && c * 8 < cols;
-  float v[8];
-  float amax = 0.f;
-  if (live) {
-    load8<BF16>(x, (size_t)row * cols + c * 8, v);
+  constexpr int RPB = kQuantThreads / LPR;  // row groups per workgroup
+  const int c = threadIdx.x % LPR;          // 8-element chunk of the row
+  const int64_t row0 = ((int64_t)blockIdx.x * RPB + threadIdx.x / LPR) * NR;
+  float v[NR][8];
+  bool live[NR];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int r = 0; r < NR; ++r) {
+    live[r] = row0 + r < rows && c * 8 < cols;
+    if (live[r]) load8<BF16>(x, (size_t)(row0 + r) * cols + c * 8, v[r]);
   }
-  // butterfly over the row's lanes (aligned groups of LPR lanes)
 #pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-  const float scale = amax > 0.f ? amax / kE4M3Max : 1.0f;
-  if (!live) return;
-  uint32_t lo = 0, hi = 0;
+  for (int r = 0; r < NR; ++r) {
+    float amax = 0.f;
+    if (live[r]) {
 #pragma unroll
-  for (int i = 0; i < 8; i += 2) {
-    const float a = fminf(fmaxf(v[i] / scale, -kE4M3Max), kE4M3Max);
-    const float b = fminf(fmaxf(v[i + 1] / scale, -kE4M3Max), kE4M3Max);
-    const uint32_t p = cvt2(a, b);
-    if (i < 4)
-      lo |= p << (8 * i);
-    else
-      hi |= p << (8 * (i - 4));
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[r][i]));
+    }
+    // butterfly over the row's lanes (aligned groups of LPR lanes)
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+    const float scale = amax > 0.f ? amax / kE4M3Max : 1.0f;
+    if (!live[r]) continue;
+    // x / scale, as its E4M3 rounding needs it: q = x * rcp(scale) is within
+    // a few float32 ulps of the correctly rounded quotient, and for |q| >=
+    // 2^-5 (E4M3 normals) the E4M3 rounding of q only depends on whether the
+    // 20 mantissa bits below E4M3's 3 lie above or below their midpoint
+    // 0x80000.  So q gives the same code as the quotient unless those bits
+    // lie within 16 of the midpoint, or |q| < 2^-5; then the lane's eight
+    // quotients are the IEEE divisions themselves.
+    // (a scale below 2^-100 takes the divisions too: its reciprocal may not
+    // be a normal float32)
+    const float rs = __builtin_amdgcn_rcpf(scale);
+    float q[8];
+    bool exact = !(scale >= 7.888609052e-31f);  // 2^-100
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      q[i] = v[r][i] * rs;
+      const uint32_t low = __builtin_bit_cast(uint32_t, q[i]) & 0xFFFFFu;
+      exact = exact || !(fabsf(q[i]) >= 0.03125f) || (low - (0x80000u - 16u)) <= 32u;
+    }
+    if (exact) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = v[r][i] / scale;
+    }
+    // (no clamp to [-448, 448]: |x| <= amax makes |q| at most a few ulps
+    // above 448, below the midpoint 464 to the next binade, so such q
+    // round to +-448 as the clamped value would)
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const uint32_t p = cvt2(q[i], q[i + 1]);
+      if (i < 4)
+        lo |= p << (8 * i);
+      else
+        hi |= p << (8 * (i - 4));
+    }
+    *reinterpret_cast<i32x2*>(codes + (size_t)(row0 + r) * cols + c * 8) = i32x2{(int)lo, (int)hi};
+    if (c == 0) scales[row0 + r] = scale;
   }
-  *reinterpret_cast<i32x2*>(codes + (size_t)row * cols + c * 8) = i32x2{(int)lo, (int)hi};
-  if (c == 0) scales[row] = scale;
 }
 
 template <bool BF16, int LPR>
 hipError_t launch_lpr(const void* x, int64_t rows, int cols, uint8_t* codes, float* scales,
                       hipStream_t stream) {
-  constexpr int RPB = kQuantThreads / LPR;
+  constexpr int NR = 4;  // rows per lane group
+  constexpr int RPB = kQuantThreads / LPR * NR;
   const int64_t blocks = (rows + RPB - 1) / RPB;
-  hipLaunchKernelGGL((fp8_quant_rows_kernel<BF16, LPR>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((fp8_quant_rows_kernel<BF16, LPR, NR>), dim3((unsigned)blocks),
                      dim3(kQuantThreads), 0, stream, x, rows, cols, codes, scales);
   return hipGetLastError();
 }

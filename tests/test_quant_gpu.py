@@ -83,6 +83,41 @@ def test_midpoints_ties_and_zero_rows(dtype):
     _assert_same(c, s, rc, rs, f"{dtype} midpoints")
 
 
+def _near_midpoint_rows():
+    # quotients x / scale a few float32 ulps either side of every E4M3
+    # midpoint, under scales that are not powers of two (and one below
+    # 2^-100): the device's fast quotient (a reciprocal product, checked
+    # against the midpoints) must agree with the IEEE division everywhere
+    vals, _ = oq.e4m3_table()
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    mids = mids[mids > 0]
+    rows = []
+    for amax in (np.float32(448 * 1.2345678), np.float32(3.7), np.float32(0.0123),
+                 np.float32(77.7), np.float32(2e-31)):
+        scale = np.float32(amax / np.float32(448))
+        for k in range(-6, 7):
+            xs = (mids * scale).astype(np.float32)
+            if k:
+                step = np.float32(np.inf) if k > 0 else np.float32(0)
+                for _ in range(abs(k)):
+                    xs = np.nextafter(xs, step).astype(np.float32)
+            xs = np.minimum(np.abs(xs), amax)
+            body = np.concatenate([xs, -xs])
+            per = 127
+            n = (len(body) + per - 1) // per
+            body = np.concatenate([body, np.zeros(n * per - len(body), np.float32)])
+            rows.append(np.concatenate([np.full((n, 1), amax, np.float32),
+                                        body.reshape(n, per)], axis=1))
+    return np.concatenate(rows).astype(np.float32)
+
+
+def test_near_midpoints_under_general_scales():
+    x = _near_midpoint_rows()
+    c, s = _quant(_dev(x, "f32"))
+    rc, rs = _oracle(x, "f32")
+    _assert_same(c, s, rc, rs, "near midpoints")
+
+
 def test_full_size_fp8_workload_q_sampled_rows():
     # Q of the fp8 workload: 8 x 4096 tokens, 32 heads, D 128, bf16 rows
     T, H, D = 8 * 4096, 32, 128
