@@ -267,7 +267,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
   // mha_fwd: key splits of its own where the longest items would set the
   // run time, partials in the workspace (laid out for batch x max_seqlen
-  // tokens; the merge stops at the real total, cu_seqlens[batch])
+  // tokens; the merge stops at the real total, cu_seqlens[batch]), the O
+  // partials in bfloat16 (half the bytes of float32 for the split kernel to
+  // write and for the merge to read)
   // (also under mha_fwd_splitkv with num_splits = 1, which is mha_fwd exactly;
   // its partial buffers are not used then)
   // (not under mha_fwd_noalloc, whose workspace holds no partials)
@@ -279,7 +281,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
     if (sp > 1) {
       num_splits = sp;
       total_tokens = (int32_t)((long long)batch * max_seqlen);  // auto_splits keeps this within int
-      part_bytes = align_up((size_t)sp * total_tokens * num_heads * v_dim * sizeof(float), 256) +
+      part_bytes = align_up((size_t)sp * total_tokens * num_heads * v_dim * sizeof(uint16_t), 256) +
                    align_up((size_t)sp * num_heads * total_tokens * sizeof(float), 256);
     }
   }
@@ -316,7 +318,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
     o_part = reinterpret_cast<float*>(ws + plan.bytes);
     lse_part = reinterpret_cast<float*>(
         ws + plan.bytes +
-        align_up((size_t)num_splits * total_tokens * num_heads * v_dim * sizeof(float), 256));
+        align_up((size_t)num_splits * total_tokens * num_heads * v_dim * sizeof(uint16_t), 256));
   }
   auto* st = direct ? nullptr : reinterpret_cast<mha::SchedState*>(ws);
   auto* table = direct ? nullptr : reinterpret_cast<mha::i32x4*>(ws + kStateBytes);
@@ -355,6 +357,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   p.o_part = num_splits > 1 ? o_part : nullptr;
   p.lse_part = num_splits > 1 ? lse_part : nullptr;
   p.max_seqlen = max_seqlen;
+  p.part_bf16 = split_here ? 1 : 0;
 
   // direct: exactly one workgroup per item of the grid (none when
   // max_seqlen is 0: every sequence is then empty or the call is refused,
@@ -376,7 +379,7 @@ int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
   }
   if (num_splits > 1) {
     // (a refused call writes no partial; the merge then writes nothing)
-    e = mha::launch_combine(o_part, lse_part, num_splits, total_tokens,
+    e = mha::launch_combine(o_part, split_here, lse_part, num_splits, total_tokens,
                             split_here ? cu_seqlens + batch : nullptr, num_heads, v_dim,
                             dtype != MHA_DTYPE_F32, o, lse, st, s);
     if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");
@@ -452,7 +455,7 @@ int mha_combine_splits(const float* o_partial, const float* lse_partial, int32_t
     return fail(MHA_ERR_INVALID_ARG, "o_partial, lse_partial, o, lse must be non-NULL");
   if (reinterpret_cast<uintptr_t>(o_partial) % 16 != 0 || reinterpret_cast<uintptr_t>(o) % 16 != 0)
     return fail(MHA_ERR_INVALID_ARG, "o_partial and o must be 16-byte aligned");
-  hipError_t e = mha::launch_combine(o_partial, lse_partial, num_splits, total_tokens, nullptr,
+  hipError_t e = mha::launch_combine(o_partial, false, lse_partial, num_splits, total_tokens, nullptr,
                                      num_heads, v_dim, out_dtype == MHA_DTYPE_BF16, o, lse,
                                      nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail_hip(e, "split-KV merge launch");

@@ -1202,22 +1202,29 @@ struct MfmaKernel {
       const float lt = half_sum(w.l);
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       if constexpr (SPLIT) {
-        // split-KV partial: float32 O over this item's key range (zero where
-        // the range holds no visible key) and its LSE (-inf there), straight
-        // from the registers: each lane writes 16-byte runs of its row
+        // split-KV partial: O over this item's key range (zero where the
+        // range holds no visible key), float32 or rounded to bfloat16, and
+        // its LSE (-inf there), straight from the registers: each lane
+        // writes runs of 4 values of its row
         const int sl = OPQ ? (int)opaque((uint32_t)lane) : 0;
         if ((OPQ ? wq0 + (sl & 31) < L : qvalid) &&
             s0 + (OPQ ? wq0 + (sl & 31) : qi) < p.part_tokens) {
           const size_t prow = ((size_t)wi.split * p.part_tokens + s0 +
                                (OPQ ? wq0 + (sl & 31) : qi)) * p.num_heads + wi.h;
           float* dst = p.o_part + prow * C::DV;
+          uint16_t* dst16 = reinterpret_cast<uint16_t*>(p.o_part) + prow * C::DV;
 #pragma unroll
           for (int t = 0; t < C::DV_TILES; ++t)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
               const f32x4 x = {w.o[t][4 * a4 + 0] * inv, w.o[t][4 * a4 + 1] * inv,
                                w.o[t][4 * a4 + 2] * inv, w.o[t][4 * a4 + 3] * inv};
-              *reinterpret_cast<f32x4*>(dst + t * 32 + 8 * a4 + 4 * (OPQ ? sl >> 5 : hf)) = x;
+              const int col = t * 32 + 8 * a4 + 4 * (OPQ ? sl >> 5 : hf);
+              if (p.part_bf16)
+                *reinterpret_cast<i32x2*>(dst16 + col) =
+                    i32x2{(int)pack_bf16x2(x[0], x[1]), (int)pack_bf16x2(x[2], x[3])};
+              else
+                *reinterpret_cast<f32x4*>(dst + col) = x;
             }
           if ((OPQ ? sl >> 5 : hf) == 0)
             p.lse_part[((size_t)wi.split * p.num_heads + wi.h) * p.part_tokens + s0 +

@@ -87,6 +87,7 @@ struct AttnParams {
   float* o_part;
   float* lse_part;
   int max_seqlen;     // the caller's bound on every sequence length
+  int part_bf16;      // o_part holds bfloat16 values instead of float32
 };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

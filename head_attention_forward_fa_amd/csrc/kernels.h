@@ -55,12 +55,13 @@ hipError_t launch_sched_visit(int batch, int num_heads, int tiles, int protocol,
 hipError_t launch_fp8_quant(const void* x, bool bf16, int64_t rows, int cols, uint8_t* codes,
                             float* scales, hipStream_t stream);
 
-// Split-KV merge (combine.hip): o_part [num_splits, T, H, Dv] float32 and
-// lse_part [num_splits, H, T] -> o [T, H, Dv] (bf16 or float32), lse [H, T].
-// With `sched` set, nothing is written when the prepass refused the call.
-hipError_t launch_combine(const float* o_part, const float* lse_part, int num_splits, int T,
-                          const int32_t* t_out, int H, int dv, bool bf16_out, void* o, float* lse,
-                          const SchedState* sched, hipStream_t stream);
+// Split-KV merge (combine.hip): o_part [num_splits, T, H, Dv] (float32, or
+// bfloat16 with part16) and lse_part [num_splits, H, T] -> o [T, H, Dv] (bf16
+// or float32), lse [H, T].  With `sched` set, nothing is written when the
+// prepass refused the call.
+hipError_t launch_combine(const void* o_part, bool part16, const float* lse_part, int num_splits,
+                          int T, const int32_t* t_out, int H, int dv, bool bf16_out, void* o,
+                          float* lse, const SchedState* sched, hipStream_t stream);
 
 // A kernel variant: its launcher and its occupancy (resident workgroups per
 // CU at its LDS and register footprint, computed once per device).

@@ -127,8 +127,9 @@ typedef enum {
  * would set the run time (few, long items for the device's CUs, e.g. one
  * long causal sequence with few heads), mha_fwd runs them as
  * mha_fwd_splitkv would, with mha_fwd_auto_splits(batch, max_seqlen,
- * num_heads, causal, v_dim, CUs) key ranges, the float32 partials in its
- * workspace, and merges them; O and LSE agree with the unsplit run up to
+ * num_heads, causal, v_dim, CUs) key ranges and the partials in its
+ * workspace (O rounded to bfloat16, LSE in float32), and merges them; O and
+ * LSE agree with the unsplit run up to that rounding of the partial O and
  * float32 rounding of the merge.  Never with fewer than 16 key blocks
  * (max_seqlen <= 960).
  *
@@ -312,8 +313,9 @@ int mha_combine_splits(const float* o_partial, const float* lse_partial, int32_t
  * the longest work item and W = the blocks of all items (causal: q-tile t of
  * 256 rows sees min(nb, 4 (t + 1)) blocks) over `cus` compute units: 1 when
  * 4 nb <= 5 ceil(W / cus), else ceil(1.2 nb / ceil(W / cus)) capped at 8 and at
- * nb / 8 (at least 8 blocks per split), lowered until the float32 partials
- * (splits x batch x max_seqlen x num_heads x v_dim x 4 bytes) fit in 1 GiB.
+ * nb / 8 (at least 8 blocks per split), lowered until splits x batch x
+ * max_seqlen x num_heads x v_dim x 4 bytes (the partial O in float32, as
+ * mha_fwd_splitkv keeps it) fit in 1 GiB.
  * The split (SM100AttentionSMem, comptime members: MiscMBarsType takes the
  * config's splitk_partitions) is the pages'; this rule for choosing it is
  * the library's.  Returns >= 1; 1 for non-positive arguments.
