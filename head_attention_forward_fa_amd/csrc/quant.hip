@@ -16,9 +16,9 @@
 // HBM-bound: each row is read once (D bf16 or float32 elements) and written
 // once (D codes + 4 bytes of scale).  A row is spread over LPR lanes (8
 // consecutive elements per lane, one 16- or 32-byte load), its amax is a
-// butterfly over those lanes, and each lane writes its 8 codes as one
-// 8-byte store, so a wave moves 64 x 16 (bf16) contiguous bytes per load
-// instruction.
+// reduction over those lanes by DPP moves and lane swaps (no LDS round
+// trips), and each lane writes its 8 codes as one 8-byte store, so a wave
+// moves 64 x 16 (bf16) contiguous bytes per load instruction.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,6 +37,33 @@ constexpr int kQuantThreads = 256;
 // even, OCP E4M3 on gfx950.
 __device__ __forceinline__ uint32_t cvt2(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// Max over each aligned group of LPR lanes (8 to 64), in every lane of the
+// group: within a row of 16 lanes by DPP moves (swap neighbours, swap pairs,
+// mirror the half-row, mirror the row), across rows by v_permlane16_swap
+// and v_permlane32_swap.  The values are magnitudes (>= 0).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+template <int LPR>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "lane group");
+  x = fmaxf(x, dpp_mov<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+  x = fmaxf(x, dpp_mov<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+  x = fmaxf(x, dpp_mov<0x141>(x));  // row_half_mirror
+  if constexpr (LPR >= 16) x = fmaxf(x, dpp_mov<0x140>(x));  // row_mirror
+  if constexpr (LPR >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if constexpr (LPR >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return x;
 }
 
 template <bool BF16>
@@ -85,9 +112,7 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_quant_rows_kernel(const voi
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[r][i]));
     }
-    // butterfly over the row's lanes (aligned groups of LPR lanes)
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+    amax = group_max<LPR>(amax);
     const float scale = amax > 0.f ? amax / kE4M3Max : 1.0f;
     if (!live[r]) continue;
     // x / scale, as its E4M3 rounding needs it: q = x * rcp(scale) is within
