@@ -133,6 +133,30 @@ def test_full_size_workloads_sampled(name):
     print(f"{name}: {len(toks)} tokens x {inp.num_heads} heads, O err {eo:.3e}, LSE err {el:.3e}")
 
 
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+def test_long_sequence_sampled(causal):
+    """One sequence of 131 072 tokens (GQA 2 / 1, D 128): far past the
+    configurations' lengths, so that token, block and table offsets run
+    large; mha_fwd splits the keys of its few long items by itself.  Rows
+    at the start, the end and around q-tile boundaries near the end, plus
+    random ones, against the oracle."""
+    S = 131072
+    inp = mi.make_inputs(dtype="bf16", seqlens=[S], num_heads=2, num_kv_heads=1,
+                         head_dim_nope=128, v_dim=128, causal=causal, seed=21)
+    print("long sequence", S, "causal" if causal else "non-causal", flush=True)
+    o, lse = run_gpu(inp)
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    rng = np.random.default_rng(5)
+    toks = {0, 1, 255, 256, S - 1, S - 2}
+    for t0 in (S - 4 * 256, S - 2 * 256, S - 256):
+        toks.update((t0 - 1, t0, t0 + 255))
+    toks.update(int(x) for x in rng.integers(0, S, 24))
+    toks = np.array(sorted(toks), dtype=np.int64)
+    ref_o, ref_lse = oracle_rows(inp, toks)
+    eo, el = _check(inp, o, lse, ref_o, ref_lse, tokens=toks)
+    print(f"long sequence: {len(toks)} tokens x 2 heads, O err {eo:.3e}, LSE err {el:.3e}")
+
+
 def test_dense_layout_equals_packed():
     inp = mi.make_inputs(dtype="bf16", seqlens=[256, 256], num_heads=4, num_kv_heads=2,
                          head_dim_nope=128, v_dim=128, causal=True, seed=3)
