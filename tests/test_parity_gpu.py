@@ -44,6 +44,11 @@ SMALL = [
     ("f32", [300, 1, 0, 129, 64], 8, 2, 64, 0, 64, False),
     ("f32", [517, 33], 4, 2, 128, 0, 128, False),
     ("f32", [260, 31], 2, 2, 128, 64, 128, False),
+    # wide query-head groups: multi-query (one KV head) and 16 per KV head
+    ("bf16", [333, 70], 32, 1, 128, 0, 128, True),
+    ("bf16", [200], 64, 4, 64, 0, 64, False),
+    ("fp8", [260], 16, 1, 128, 0, 128, True),
+    ("bf16", [150], 16, 1, 128, 64, 128, True),
     # more items than workgroups (about 1 000 against 256): every workgroup
     # runs several items in a row, so whatever an item carries over to the
     # next (its Q fragments, the fp8 q_scale multiplier, the next item's
