@@ -138,6 +138,20 @@ def test_full_size_workloads_sampled(name):
     print(f"{name}: {len(toks)} tokens x {inp.num_heads} heads, O err {eo:.3e}, LSE err {el:.3e}")
 
 
+@pytest.mark.parametrize("dtype,dn,dr,scale", [("bf16", 128, 0, 0.31), ("bf16", 128, 64, 0.02),
+                                               ("fp8", 128, 0, 0.4), ("f32", 64, 0, 1.7)])
+def test_explicit_softmax_scale(dtype, dn, dr, scale):
+    """A softmax scale other than 1/sqrt(Dn + Dr) reaches every kernel (large
+    scales sharpen the rows, small ones flatten them)."""
+    inp = mi.make_inputs(dtype=dtype, seqlens=[300, 41], num_heads=4, num_kv_heads=2,
+                         head_dim_nope=dn, head_dim_rope=dr, v_dim=dn, causal=True, seed=17,
+                         softmax_scale=scale)
+    print("scale", dtype, dn, dr, scale, flush=True)
+    o, lse = run_gpu(inp)
+    ref_o, ref_lse = oracle_full(inp)
+    _check(inp, o, lse, ref_o, ref_lse)
+
+
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
 def test_long_sequence_sampled(causal):
     """One sequence of 131 072 tokens (GQA 2 / 1, D 128): far past the
