@@ -158,6 +158,12 @@ struct MfmaCfg {
   static constexpr int DV_TILES = DV / 32;
   static constexpr int NPV = 2 * DV_TILES;  // P V products per sub-tile
   static constexpr int G_AHEAD = 2;         // products between an operand read and its use
+  // The first KPF S operand fragments of a product half-step are read at
+  // the start of the softmax half-step before it, whose vector work then
+  // covers their latency (a wave reads LDS at a limited rate, and does not
+  // read it at all in its softmax half-steps otherwise).  Two measured best
+  // on the bf16 layouts (three and four gained less); the others keep none.
+  static constexpr int KPF = (!FP8 && DR == 0) ? 2 : 0;
   // 1 KiB DMA instructions per block and region.  The waves of group 0
   // (DW of them, one per SIMD) issue them: wave w takes instructions w,
   // w + DW, ... of each region (the fp8 k_scale: wave 0, one dword per
@@ -718,13 +724,14 @@ struct MfmaKernel {
 
   // Matrix-core half-step: P V of sub-tile i (P in w.pw, V rows in half VH
   // of the V block at vb) and S of sub-tile i+1 (K rows in half KH of the K
-  // block at kb / rb) into w.st; the S of a sub-tile
-  // past the wave's last is computed from whatever the slot holds and never
-  // used.
+  // block at kb / rb, the first KPF of its fragments already in kpre) into
+  // w.st; the S of a sub-tile past the wave's last is computed from
+  // whatever the slot holds and never used.
   template <int KH, int VH>
   static __device__ __forceinline__ void gphase(State& w, uint32_t kb, uint32_t rb,
                                                 const uint32_t (&vb)[C::DV_TILES],
-                                                const QFrag* qf, const bf16x8* qr) {
+                                                const QFrag* qf, const bf16x8* qr,
+                                                const QFrag* kpre) {
     // K rows of half KH of the K block, V rows of half VH of the V block
     const uint32_t kn = kb + KH * 32 * C::K_RP, rn = rb + KH * 32 * C::R_RP;
     uint32_t vh[C::DV_TILES];
@@ -756,7 +763,10 @@ struct MfmaKernel {
       } else if constexpr (C::MIXED && idx >= C::QK_STEPS) {
         srn = r_mfma(r_frag(rn, idx - C::QK_STEPS), qr[idx - C::QK_STEPS], srn);
       } else {
-        sn = s_mfma(s_frag(kn, rn, idx), qf[idx], sn);
+        if constexpr (idx < C::KPF)
+          sn = s_mfma(kpre[idx], qf[idx], sn);
+        else
+          sn = s_mfma(s_frag(kn, rn, idx), qf[idx], sn);
       }
     });
     // Slot shape for the machine scheduler: each product's operands are
@@ -769,8 +779,9 @@ struct MfmaKernel {
       if constexpr (k < NS) {
         constexpr bool PV = k < 2 * NPAIR ? (k % 2 == 0) : (C::NPV > C::S_STEPS);
         constexpr int idx = k < 2 * NPAIR ? k / 2 : k - NPAIR;
-        __builtin_amdgcn_sched_group_barrier(0x100, PV ? 2 : (C::F8MMA && idx < C::QK_STEPS ? 2 : 1),
-                                             0);
+        if constexpr (PV || idx >= C::KPF)
+          __builtin_amdgcn_sched_group_barrier(
+              0x100, PV ? 2 : (C::F8MMA && idx < C::QK_STEPS ? 2 : 1), 0);
       }
       if constexpr (k >= RA) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     });
@@ -1092,8 +1103,18 @@ struct MfmaKernel {
       // softmax half-step of sub-tile i = 2j + H (k_scale from K block j);
       // group 0 also issues its share of the block's DMA.  CHK: the sub-tile
       // may be missing or be the wave's last (masked).
+      QFrag kpre[C::KPF > 0 ? C::KPF : 1];
       auto xh = [&](auto grpc, auto chk, auto part, int i, int j, const BlockDma& bd) {
         constexpr int H = decltype(part)::value;
+        if constexpr (C::KPF > 0) {
+          // the next product half-step's first S operands: half 1 of K block
+          // j after X_{2j}, half 0 of block j + 1 after X_{2j+1}
+          const int jk = H == 0 ? j : j + 1;
+          const uint32_t kn = opaque(sbase + (uint32_t)(jk % C::NKS) * C::KSLOT + C::K_OFF + ln.k) +
+                              (H == 0 ? 32 * C::K_RP : 0);
+#pragma unroll
+          for (int s = 0; s < C::KPF; ++s) kpre[s] = s_frag(kn, 0u, s);
+        }
         constexpr bool DMA = decltype(grpc)::value == 0;
         constexpr int O0 = !DMA ? 0 : H == 0 ? 0 : OPH;
         constexpr int O1 = !DMA ? 0 : H == 0 ? OPH : C::N_OPS;
@@ -1119,7 +1140,7 @@ struct MfmaKernel {
           for (int t = 0; t < C::DV_TILES; ++t) vb[t] = opaque(vs + ln.v[t]);
           gphase<decltype(kh)::value, decltype(vh_)::value>(
               w, opaque(ks + C::K_OFF + ln.k), C::DR > 0 ? opaque(ks + C::R_OFF + ln.r) : 0u, vb,
-              qf, qr);
+              qf, qr, kpre);
         }
       };
       using P0 = std::integral_constant<int, 0>;
