@@ -911,8 +911,9 @@ struct MfmaKernel {
         const int r = QRPI * i + ql / QCPR, c = ql % QCPR;
         i32x4 x = {0, 0, 0, 0};
         if (r0 + r < nw.L)
-          x = *reinterpret_cast<const i32x4*>(
-              qp + (((size_t)(nw.s0 + r0 + r) * p.num_heads + nw.h) * C::DN) * 2 + c * 16);
+          // (read once per item: a streaming load, as for the output)
+          x = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(
+              qp + (((size_t)(nw.s0 + r0 + r) * p.num_heads + nw.h) * C::DN) * 2 + c * 16));
         if constexpr (QROWS) qf_x[i] = __builtin_bit_cast(bf16x8, x);
       }
       cq_x = p.scale_log2;
@@ -1284,8 +1285,11 @@ struct MfmaKernel {
         if (row < L) {
           const i32x4 x =
               *reinterpret_cast<const i32x4*>(smem + (wave * 32 + r) * C::O_ROW + cc * 16);
-          *reinterpret_cast<i32x4*>(op + (((size_t)(s0 + row) * p.num_heads + wi.h) * C::DV) * 2 +
-                                    cc * 16) = x;
+          // (write-once output: a streaming store, which leaves the L2 to
+          // the K/V blocks that later items of the same head read again)
+          __builtin_nontemporal_store(
+              x, reinterpret_cast<i32x4*>(
+                     op + (((size_t)(s0 + row) * p.num_heads + wi.h) * C::DV) * 2 + cc * 16));
         }
       }
       if constexpr (QROWS) place_q_rows();
