@@ -69,7 +69,10 @@ __device__ __forceinline__ float group_max(float x) {
 template <bool BF16>
 __device__ __forceinline__ void load8(const void* x, size_t elem, float (&v)[8]) {
   if constexpr (BF16) {
-    const i32x4 w = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(x) + elem);
+    // (input read once, codes written once: streaming accesses, which keep
+    // them from displacing what the L2 holds for other work)
+    const i32x4 w =
+        __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(x) + elem));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = __builtin_bit_cast(float, (uint32_t)w[i] << 16);
@@ -149,7 +152,8 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_quant_rows_kernel(const voi
       else
         hi |= p << (8 * (i - 4));
     }
-    *reinterpret_cast<i32x2*>(codes + (size_t)(row0 + r) * cols + c * 8) = i32x2{(int)lo, (int)hi};
+    __builtin_nontemporal_store(i32x2{(int)lo, (int)hi},
+                                reinterpret_cast<i32x2*>(codes + (size_t)(row0 + r) * cols + c * 8));
     if (c == 0) scales[row0 + r] = scale;
   }
 }
